@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Decode QMV benchmark on one MI355X.
+
+Workload (one step): the decode QMV of one hidden=5120 decoder layer at M=1
+-- the seven projection shapes (q 6144x5120, k/v 1024x5120, o 5120x6144,
+gate/up 17408x5120, down 5120x17408) -- for bits 1 and 2 and group sizes 64
+and 128 (28 calls, affine weights with stored biases).  Inputs are seeded
+synthetic tensors already resident in HBM; two distinct copies alternate
+between steps so that the 256 MB last-level cache cannot serve the weights.
+
+value = algorithmic bytes of a step (packed W + scales + biases + x + y)
+        / measured step time, in GB/s.
+
+Each step is one HIP graph replay (the graph holds the 28 launches), so
+launch overhead from Python is not in the timed region.
+
+Extra objects on the JSON line:
+  roofline      the dominant kernel (2-bit, gs=64, M=1) over its seven shapes:
+                algorithmic bytes per launch / average launch duration from
+                HIP events around graph replays of just those launches.
+  cpu_baseline  the fp64 CPU oracle on a bounded sample (see --cpu-sample).
+  breakdown     per (bits, gs, shape) microseconds and GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QMV achieved HBM GB/s (W+scales+biases+x) at M=1..5; % of MI355X peak"
+PEAK_HBM_GBS = 8000.0
+SHAPES = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", default="q,k,v,o,down",
+                    help="shapes (2-bit, gs=64, M=1) timed with the CPU oracle")
+    ap.add_argument("--suite", default="", help="'full': also time M=1..5 wide/sym, t5 and qmm "
+                    "configurations and write them to --detail-csv")
+    ap.add_argument("--detail-csv", default=os.path.join(ROOT, "gpurun_out", "bench_detail.csv"))
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup + steps only (for rocprofv3), skip the extra measurements")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(fmt, M, N, K, gs, bias_stored):
+    G = K // gs
+    if fmt == "t5":
+        w = N * G * ((gs + 4) // 5)
+    else:
+        w = N * K * (1 if fmt == "u1" else 2) // 8
+    return w + N * G * 2 * (2 if bias_stored else 1) + M * K * 2 + M * N * 2
+
+
+class Call:
+    """One C ABI call on device-resident inputs."""
+
+    def __init__(self, entry, fmt, M, N, K, gs, tensors, label):
+        self.entry, self.fmt, self.M, self.N, self.K, self.gs = entry, fmt, M, N, K, gs
+        self.t = tensors  # keep alive
+        self.label = label
+        x, w, s, b, y = tensors
+        self.ptrs = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None,
+                     y.data_ptr())
+        self.bits = {"u1": 1, "u2": 2, "t5": 0}[fmt]
+        self.bytes = algorithmic_bytes(fmt, M, N, K, gs, b is not None and entry != "bq_qmv_sym")
+
+    def launch(self, lib, stream):
+        x, w, s, b, y = self.ptrs
+        st = getattr(lib, self.entry)(x, w, s, b, y, self.M, self.N, self.K, self.bits, self.gs, stream)
+        if st != 0:
+            raise RuntimeError(f"{self.entry} {self.label}: status {st}")
+
+
+def upload(torch, a, dev):
+    import numpy as np
+    if a is None:
+        return None
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def make_calls(torch, dev, specs, copies):
+    """specs: list of (entry, fmt, M, N, K, gs, variant, label).  Returns
+    calls[copy][i] with distinct device buffers per copy."""
+    import synth
+    out = [[] for _ in range(copies)]
+    for (entry, fmt, M, N, K, gs, variant, label) in specs:
+        inp = synth.make_inputs(fmt, M, N, K, gs, variant, seed=0)
+        for c in range(copies):
+            x = upload(torch, inp.x, dev)
+            w = upload(torch, inp.w, dev)
+            s = upload(torch, inp.scales, dev)
+            b = upload(torch, inp.biases, dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            out[c].append(Call(entry, fmt, M, N, K, gs, (x, w, s, b, y), label))
+    return out
+
+
+def capture(torch, lib, calls, reps=1):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        for _ in range(reps):
+            for c in calls:
+                c.launch(lib, h)
+    return g
+
+
+def time_graphs(torch, graphs, replays):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(replays):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3  # seconds
+
+
+def per_call_seconds(torch, lib, call_copies, launches=40, replays=5):
+    """Average duration of one call: graph of `launches` back-to-back launches
+    alternating between buffer copies, replayed `replays` times."""
+    seq = [call_copies[i % len(call_copies)] for i in range(launches)]
+    g = capture(torch, lib, seq)
+    g.replay()
+    t = time_graphs(torch, [g], replays)
+    return t / (launches * replays)
+
+
+def cpu_baseline(shapes):
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    total_bytes, total_t = 0, 0.0
+    for shape in shapes:
+        N, K = synth.PROJECTION_SHAPES[shape]
+        inp = synth.make_inputs("u2", 1, N, K, 64, "asym", seed=0)
+        t0 = time.perf_counter()
+        y, _ = oracle.qmv_reference("u2", inp.x, inp.w, inp.scales, inp.biases, K, 64)
+        total_t += time.perf_counter() - t0
+        total_bytes += algorithmic_bytes("u2", 1, N, K, 64, True)
+        del y
+    return {
+        "value": round(total_bytes / total_t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle (unpack, dequantize, x@W^T), 2-bit gs=64 M=1, shapes {','.join(shapes)}: "
+                  f"{total_bytes / 1e6:.1f} MB in {total_t:.2f} s; host cores visible "
+                  f"{len(os.sched_getaffinity(0))}, BLAS threads {blas_threads}",
+    }
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_decode_qmv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM traffic per launch from committed counter runs, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        rec = data.get(kernel_key)
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            return rec.get("bytes_per_launch")
+    except Exception:  # noqa: BLE001
+        return None
+    return None
+
+
+def full_suite(torch, lib, dev, path):
+    import synth
+    rows = []
+    specs = []
+    for fmt in ("u1", "u2"):
+        for gs in (64, 128):
+            for M in (1, 2, 3, 4, 5):
+                for variant, entry in (("asym", "bq_qmv_wide"), ("sym", "bq_qmv_sym")):
+                    for shape in SHAPES:
+                        N, K = synth.PROJECTION_SHAPES[shape]
+                        specs.append((entry, fmt, M, N, K, gs, variant, shape))
+                for shape in ("gate", "down"):  # W read M times
+                    N, K = synth.PROJECTION_SHAPES[shape]
+                    specs.append(("bq_qmv", fmt, M, N, K, gs, "asym", shape))
+    for gs in (64, 128):
+        for M in (1, 2, 3, 4, 5):
+            for shape in SHAPES:
+                N, K = synth.PROJECTION_SHAPES[shape]
+                specs.append(("bq_t5_qmv_wide", "t5", M, N, K, gs, "t5", shape))
+    qmm_specs = []
+    for M in (32, 512, 2048):
+        for shape in ("gate", "down"):
+            N, K = synth.PROJECTION_SHAPES[shape]
+            qmm_specs.append(("bq_t5_qmm", "t5", M, N, K, 128, "t5", shape))
+    with open(path, "w") as f:
+        f.write("entry,fmt,variant,M,shape,N,K,gs,us,GBps,frac_hbm,TFLOPs\n")
+        for spec in specs + qmm_specs:
+            copies = make_calls(torch, dev, [spec], 2)
+            pair = [copies[0][0], copies[1][0]]
+            launches = 8 if spec[0] == "bq_t5_qmm" and spec[2] >= 512 else 40
+            t = per_call_seconds(torch, lib, pair, launches=launches, replays=3)
+            c = pair[0]
+            gbs = c.bytes / t / 1e9
+            tflops = (2.0 * c.M * c.N * c.K / t / 1e12) if spec[0] == "bq_t5_qmm" else 0.0
+            line = (f"{spec[0]},{spec[1]},{spec[6]},{spec[2]},{spec[7]},{spec[3]},{spec[4]},{spec[5]},"
+                    f"{t * 1e6:.3f},{gbs:.1f},{gbs / PEAK_HBM_GBS:.4f},{tflops:.1f}")
+            f.write(line + "\n")
+            f.flush()
+            print(line, file=sys.stderr, flush=True)
+            rows.append(line)
+            del copies, pair
+            torch.cuda.empty_cache()
+    return rows
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the QMV path has no multi-GPU mode in this build "
+              "(it would shard W along N with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_decode_qmv_amd as bq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = bq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    specs = []
+    for bits in (1, 2):
+        fmt = "u1" if bits == 1 else "u2"
+        for gs in (64, 128):
+            for shape in SHAPES:
+                N, K = synth.PROJECTION_SHAPES[shape]
+                specs.append(("bq_qmv", fmt, 1, N, K, gs, "asym", f"{fmt}/gs{gs}/{shape}"))
+    print(f"bench: generating {len(specs)} calls x 2 copies", file=sys.stderr, flush=True)
+    copies = make_calls(torch, dev, specs, 2)
+    step_bytes = sum(c.bytes for c in copies[0])
+
+    # eager warm-up (loads the code object before any capture)
+    h = torch.cuda.current_stream().cuda_stream
+    for cs in copies:
+        for c in cs:
+            c.launch(lib, h)
+    torch.cuda.synchronize()
+
+    graphs = [capture(torch, lib, cs) for cs in copies]
+    for i in range(args.warmup):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    elapsed = time_graphs(torch, graphs, args.steps)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode QMV M=1, 7 projection shapes of a hidden=5120 decoder, bits {1,2} x "
+                        "group_size {64,128}, affine (stored biases)",
+            "M": 1,
+            "calls_per_step": len(specs),
+            "bytes_per_step": step_bytes,
+            "parallelism": "single GPU",
+        },
+    }
+
+    if not args.profile_only:
+        # dominant kernel: 2-bit, gs=64, M=1 affine, over its seven shapes
+        dom = [i for i, c in enumerate(copies[0]) if c.fmt == "u2" and c.gs == 64]
+        seq = []
+        for rep in range(4):
+            for i in dom:
+                seq.append(copies[rep % 2][i])
+        gd = capture(torch, lib, seq)
+        gd.replay()
+        reps = 10
+        t = time_graphs(torch, [gd], reps)
+        avg_launch = t / (reps * len(seq))
+        bytes_per_launch = sum(copies[0][i].bytes for i in dom) / len(dom)
+        achieved = bytes_per_launch / avg_launch / 1e9
+        result["roofline"] = {
+            "bound": "hbm",
+            "kernel": "qmv_kernel<2-bit, gs=64, M=1, stored bias>",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("qmv_u2_gs64_m1"),
+            "avg_launch_us": round(avg_launch * 1e6, 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+        }
+        bd = {}
+        for i, c in enumerate(copies[0]):
+            ts = per_call_seconds(torch, lib, [copies[0][i], copies[1][i]], launches=20, replays=3)
+            bd[c.label] = {"us": round(ts * 1e6, 2), "GBps": round(c.bytes / ts / 1e9, 1)}
+        result["breakdown"] = bd
+        if args.suite == "full":
+            os.makedirs(os.path.dirname(args.detail_csv), exist_ok=True)
+            del graphs, gd
+            full_suite(torch, lib, dev, args.detail_csv)
+        if not args.no_cpu_baseline:
+            shapes = [s for s in args.cpu_sample.split(",") if s]
+            print(f"bench: cpu oracle on {shapes}", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = cpu_baseline(shapes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

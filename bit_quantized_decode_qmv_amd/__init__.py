@@ -1,0 +1,213 @@
+"""Low-bit weight-quantized decode QMV for MI355X (gfx950).
+
+Thin binding over the C ABI of ``libbq.so`` (declared in ``include/bq.h``):
+argument marshalling only -- every step of the product runs in the HIP
+kernels.  PyTorch is used for device memory and streams.
+
+Two layers:
+
+* ``bq_*`` functions with the C names and C arguments (integers for
+  pointers and the stream); they raise :class:`BQError` on a nonzero status.
+* tensor helpers (``qmv``, ``qmv_wide``, ``qmv_sym``, ``t5_qmv``,
+  ``t5_qmv_wide``, ``t5_qmm``, ``dequant``) that check devices, dtypes and
+  contiguity, allocate the output and pass the current stream.
+
+The library is loaded on first use; a missing build or an ABI mismatch is an
+error (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+ABI_VERSION = 1
+BITS_T5 = 0
+MAX_WIDE_M = 5
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
+
+ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
+                "bq_t5_qmm", "bq_dequant")
+ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS
+
+STATUS = {
+    0: "BQ_OK", -1: "BQ_ERR_NULL", -2: "BQ_ERR_BITS", -3: "BQ_ERR_GROUP", -4: "BQ_ERR_SHAPE",
+    -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP",
+}
+
+
+class BQError(RuntimeError):
+    def __init__(self, status: int, message: str, entry: str):
+        super().__init__(f"{entry}: {STATUS.get(status, status)} ({message})")
+        self.status = status
+        self.entry = entry
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libbq.so once and check its ABI version."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    lib.bq_abi_version.restype = ctypes.c_int
+    lib.bq_abi_version.argtypes = []
+    lib.bq_strerror.restype = ctypes.c_char_p
+    lib.bq_strerror.argtypes = [ctypes.c_int]
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ENTRY_POINTS:
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    ver = lib.bq_abi_version()
+    if ver != ABI_VERSION:
+        raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().bq_strerror(status).decode()
+
+
+def _call(name: str, x, w, scales, biases, y, M, N, K, bits, group_size, stream) -> int:
+    lib = load_library()
+    st = getattr(lib, name)(x, w, scales, biases, y, M, N, K, bits, group_size, stream)
+    if st != 0:
+        raise BQError(st, lib.bq_strerror(st).decode(), name)
+    return st
+
+
+def _c_entry(name):
+    def fn(x, w, scales, biases, y, M, N, K, bits, group_size, stream=None):
+        return _call(name, x, w, scales, biases, y, M, N, K, bits, group_size, stream)
+    fn.__name__ = name
+    fn.__doc__ = f"C entry point {name} of include/bq.h (pointers and stream as integers)."
+    return fn
+
+
+bq_qmv = _c_entry("bq_qmv")
+bq_qmv_wide = _c_entry("bq_qmv_wide")
+bq_qmv_sym = _c_entry("bq_qmv_sym")
+bq_t5_qmv = _c_entry("bq_t5_qmv")
+bq_t5_qmv_wide = _c_entry("bq_t5_qmv_wide")
+bq_t5_qmm = _c_entry("bq_t5_qmm")
+bq_dequant = _c_entry("bq_dequant")
+
+
+def bq_abi_version() -> int:
+    return load_library().bq_abi_version()
+
+
+# ---------------------------------------------------------------------------
+# torch helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _run(name, x, w, scales, biases, bits, group_size, out, M, N, K, out_shape):
+    torch = _torch()
+    dev = w.device
+    _check(w, "w", torch.uint8 if bits == BITS_T5 else torch.int32, dev)
+    _check(scales, "scales", torch.float16, dev)
+    if biases is not None:
+        _check(biases, "biases", torch.float16, dev)
+    if x is not None:
+        _check(x, "x", torch.float16, dev)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.float16, device=dev)
+    else:
+        _check(out, "out", torch.float16, dev)
+        if tuple(out.shape) != tuple(out_shape):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(out_shape)}")
+    _call(name, x.data_ptr() if x is not None else None, w.data_ptr(), scales.data_ptr(),
+          biases.data_ptr() if biases is not None else None, out.data_ptr(), M, N, K, bits,
+          group_size, _stream_handle(dev))
+    return out
+
+
+def _shapes(x, scales, group_size):
+    M, K = x.shape
+    N = scales.shape[0]
+    if scales.shape[1] * group_size != K:
+        raise ValueError("scales must be [N][K/group_size]")
+    return M, N, K
+
+
+def qmv(x, w, scales, biases, bits: int, group_size: int, out=None):
+    """y = x . W^T, each row of x an independent pass over W (bits 1 or 2)."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_qmv", x, w, scales, biases, bits, group_size, out, M, N, K, (M, N))
+
+
+def qmv_wide(x, w, scales, biases, bits: int, group_size: int, out=None):
+    """y = x . W^T for 1..5 rows sharing one read of W (bits 1 or 2)."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_qmv_wide", x, w, scales, biases, bits, group_size, out, M, N, K, (M, N))
+
+
+def qmv_sym(x, w, scales, bits: int, group_size: int, out=None, biases=None):
+    """Symmetric variant: bias implied as -scale*(2^bits-1)/2, never read."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_qmv_sym", x, w, scales, biases, bits, group_size, out, M, N, K, (M, N))
+
+
+def t5_qmv(x, w, scales, group_size: int, biases=None, out=None):
+    """t5 ternary weights, each row of x an independent pass."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_t5_qmv", x, w, scales, biases, BITS_T5, group_size, out, M, N, K, (M, N))
+
+
+def t5_qmv_wide(x, w, scales, group_size: int, biases=None, out=None):
+    """t5 ternary weights, 1..5 rows sharing one read of W."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_t5_qmv_wide", x, w, scales, biases, BITS_T5, group_size, out, M, N, K, (M, N))
+
+
+def t5_qmm(x, w, scales, group_size: int, biases=None, out=None):
+    """t5 prefill product on the matrix cores (any M)."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_t5_qmm", x, w, scales, biases, BITS_T5, group_size, out, M, N, K, (M, N))
+
+
+def dequant(w, scales, biases, bits: int, group_size: int, K: int, out=None):
+    """fp16 [N][K] weights, each the correctly rounded scale*q + bias."""
+    N = scales.shape[0]
+    return _run("bq_dequant", None, w, scales, biases, bits, group_size, out, 0, N, K, (N, K))
+
+
+__all__ = [
+    "ABI_VERSION", "ALL_SYMBOLS", "BITS_T5", "BQError", "ENTRY_POINTS", "LIB_PATH", "MAX_WIDE_M",
+    "bq_abi_version", "bq_dequant", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_t5_qmm",
+    "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "load_library", "qmv", "qmv_sym", "qmv_wide",
+    "strerror", "t5_qmm", "t5_qmv", "t5_qmv_wide",
+]

@@ -1,0 +1,235 @@
+// C ABI of the library: argument validation, kernel selection and launch.
+// Declarations and the meaning of every argument are in include/bq.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bq.h"
+#include "dequant_kernels.hpp"
+#include "qmm_kernels.hpp"
+#include "qmv_kernels.hpp"
+
+namespace {
+
+using namespace bq;
+
+enum Entry { E_QMV, E_WIDE, E_SYM, E_T5, E_T5_WIDE, E_QMM, E_DEQUANT };
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int row_bytes_of(int bits, int K, int gs) {
+  if (bits == BQ_BITS_T5) return (K / gs) * ((gs + 4) / 5);
+  return K / 8 * bits;
+}
+
+int validate(Entry e, const void* x, const void* w, const void* scales, const void* biases,
+             const void* y, int M, int N, int K, int bits, int gs) {
+  const bool t5 = (e == E_T5 || e == E_T5_WIDE || e == E_QMM);
+  if (!w || !scales || !y) return BQ_ERR_NULL;
+  if (e != E_DEQUANT && !x) return BQ_ERR_NULL;
+  if ((e == E_QMV || e == E_WIDE) && !biases) return BQ_ERR_NULL;
+  if (e == E_DEQUANT) {
+    if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
+  } else if (t5) {
+    if (bits != BQ_BITS_T5) return BQ_ERR_BITS;
+  } else if (bits != 1 && bits != 2) {
+    return BQ_ERR_BITS;
+  }
+  if (gs != 64 && gs != 128) return BQ_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % gs != 0 || K > (1 << 30)) return BQ_ERR_SHAPE;
+  if (e != E_DEQUANT) {
+    if (M < 1) return BQ_ERR_M;
+    if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
+  }
+  if (!aligned(w, 4) || !aligned(scales, 2) || (biases && !aligned(biases, 2))) return BQ_ERR_ALIGN;
+  if (x && !aligned(x, 2)) return BQ_ERR_ALIGN;
+  if (!aligned(y, 2)) return BQ_ERR_ALIGN;
+  if (bits == BQ_BITS_T5 && K % 256 != 0) return BQ_ERR_ALIGN;
+  if (e == E_QMM && !aligned(x, 16)) return BQ_ERR_ALIGN;
+  if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
+  return BQ_OK;
+}
+
+int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, void* params) {
+  void* args[] = {params};
+  hipError_t err = hipLaunchKernel(fn, grid, block, args, shmem, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? BQ_OK : BQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- qmv family
+// Rows per slot kept in registers, per M.
+template <int M> constexpr int rcap() { return M <= 2 ? 4 : (M <= 4 ? 3 : 2); }
+
+template <int FMT, int GS, int M, bool IMPLIED>
+int launch_qmv_t(QmvParams p, void* stream) {
+  using F = Fmt<FMT, GS>;
+  constexpr int R = rcap<M>();
+  constexpr int SLOTS = kWaves * (64 / F::KL);
+  constexpr int TC = kTile / F::CH;
+  const size_t shmem = (size_t)(2 * M * TC * F::XD + 2 * M * TC) * sizeof(uint32_t);
+  p.rows_per_wg = SLOTS * R;
+  dim3 grid((p.N + p.rows_per_wg - 1) / p.rows_per_wg);
+  return launch(reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, R>), grid,
+                dim3(kThreads), shmem, stream, &p);
+}
+
+typedef int (*QmvLauncher)(QmvParams, void*);
+
+template <int FMT, int GS, bool IMPLIED>
+QmvLauncher pick_m(int M) {
+  switch (M) {
+    case 1: return &launch_qmv_t<FMT, GS, 1, IMPLIED>;
+    case 2: return &launch_qmv_t<FMT, GS, 2, IMPLIED>;
+    case 3: return &launch_qmv_t<FMT, GS, 3, IMPLIED>;
+    case 4: return &launch_qmv_t<FMT, GS, 4, IMPLIED>;
+    case 5: return &launch_qmv_t<FMT, GS, 5, IMPLIED>;
+  }
+  return nullptr;
+}
+
+QmvLauncher pick_qmv(int fmt, int gs, int M, bool implied) {
+  if (fmt == FMT_U1) {
+    if (gs == 64) return implied ? pick_m<FMT_U1, 64, true>(M) : pick_m<FMT_U1, 64, false>(M);
+    return implied ? pick_m<FMT_U1, 128, true>(M) : pick_m<FMT_U1, 128, false>(M);
+  }
+  if (fmt == FMT_U2) {
+    if (gs == 64) return implied ? pick_m<FMT_U2, 64, true>(M) : pick_m<FMT_U2, 64, false>(M);
+    return implied ? pick_m<FMT_U2, 128, true>(M) : pick_m<FMT_U2, 128, false>(M);
+  }
+  if (gs == 64) return implied ? pick_m<FMT_T5, 64, true>(M) : pick_m<FMT_T5, 64, false>(M);
+  return implied ? pick_m<FMT_T5, 128, true>(M) : pick_m<FMT_T5, 128, false>(M);
+}
+
+// rows_at_once: M for the wide entry points, 1 for the per-row ones.
+int run_qmv(Entry e, const void* x, const void* w, const void* scales, const void* biases, void* y,
+            int M, int N, int K, int bits, int gs, void* stream) {
+  int st = validate(e, x, w, scales, biases, y, M, N, K, bits, gs);
+  if (st != BQ_OK) return st;
+  const bool t5 = (bits == BQ_BITS_T5);
+  const int fmt = t5 ? FMT_T5 : (bits == 1 ? FMT_U1 : FMT_U2);
+  const bool implied = (e == E_SYM) || (t5 && biases == nullptr);
+  QmvParams p{};
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = static_cast<const half_t*>(scales);
+  p.b = implied ? nullptr : static_cast<const half_t*>(biases);
+  p.N = N;
+  p.K = K;
+  p.G = K / gs;
+  p.row_bytes = row_bytes_of(bits, K, gs);
+  p.ratio = t5 ? 1.0f : (bits == 1 ? 0.5f : 1.5f);
+  const bool per_row = (e == E_QMV || e == E_T5);
+  const int rows_at_once = per_row ? 1 : M;
+  QmvLauncher fn = pick_qmv(fmt, gs, rows_at_once, implied);
+  if (!fn) return BQ_ERR_M;
+  for (int m0 = 0; m0 < M; m0 += rows_at_once) {
+    p.x = static_cast<const half_t*>(x) + (size_t)m0 * K;
+    p.y = static_cast<half_t*>(y) + (size_t)m0 * N;
+    st = fn(p, stream);
+    if (st != BQ_OK) return st;
+  }
+  return BQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bq_abi_version(void) { return BQ_ABI_VERSION; }
+
+const char* bq_strerror(int status) {
+  switch (status) {
+    case BQ_OK: return "success";
+    case BQ_ERR_NULL: return "a required pointer is NULL";
+    case BQ_ERR_BITS: return "bits is not valid for this entry point (1, 2, or BQ_BITS_T5 = 0)";
+    case BQ_ERR_GROUP: return "group_size must be 64 or 128";
+    case BQ_ERR_SHAPE: return "N and K must be positive, K a multiple of group_size and at most 2^30";
+    case BQ_ERR_M: return "M is outside the range this entry point accepts";
+    case BQ_ERR_ALIGN: return "a pointer is misaligned, or a t5 call has K not a multiple of 256";
+    case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+  }
+  return "unknown bq status";
+}
+
+int bq_qmv(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+           int N, int K, int bits, int group_size, void* stream) {
+  return run_qmv(E_QMV, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+int bq_qmv_wide(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                int M, int N, int K, int bits, int group_size, void* stream) {
+  return run_qmv(E_WIDE, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+int bq_qmv_sym(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+               int N, int K, int bits, int group_size, void* stream) {
+  return run_qmv(E_SYM, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+int bq_t5_qmv(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+              int N, int K, int bits, int group_size, void* stream) {
+  return run_qmv(E_T5, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+int bq_t5_qmv_wide(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                   int M, int N, int K, int bits, int group_size, void* stream) {
+  return run_qmv(E_T5_WIDE, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+              int N, int K, int bits, int group_size, void* stream) {
+  int st = validate(E_QMM, x, w, scales, biases, y, M, N, K, bits, group_size);
+  if (st != BQ_OK) return st;
+  QmmParams p{};
+  p.x = static_cast<const half_t*>(x);
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = static_cast<const half_t*>(scales);
+  p.b = static_cast<const half_t*>(biases);
+  p.y = static_cast<half_t*>(y);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.G = K / group_size;
+  p.gs = group_size;
+  p.row_bytes = row_bytes_of(BQ_BITS_T5, K, group_size);
+  dim3 grid((N + kQmmBN - 1) / kQmmBN, (M + kQmmBM - 1) / kQmmBM);
+  const void* fn = biases ? reinterpret_cast<const void*>(&t5_qmm_kernel<false>)
+                          : reinterpret_cast<const void*>(&t5_qmm_kernel<true>);
+  return launch(fn, grid, dim3(256), 0, stream, &p);
+}
+
+int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+               int N, int K, int bits, int group_size, void* stream) {
+  int st = validate(E_DEQUANT, x, w, scales, biases, y, M, N, K, bits, group_size);
+  if (st != BQ_OK) return st;
+  DequantParams p{};
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = static_cast<const half_t*>(scales);
+  p.b = static_cast<const half_t*>(biases);
+  p.out = static_cast<half_t*>(y);
+  p.N = N;
+  p.K = K;
+  p.G = K / group_size;
+  p.gs = group_size;
+  p.row_bytes = row_bytes_of(bits, K, group_size);
+  p.ratio = bits == BQ_BITS_T5 ? 1.0f : (bits == 1 ? 0.5f : 1.5f);
+  const bool implied = (biases == nullptr);
+  size_t items;
+  const void* fn;
+  if (bits == BQ_BITS_T5) {
+    items = (size_t)N * p.G * ((group_size + 4) / 5);
+    fn = implied ? reinterpret_cast<const void*>(&dequant_t5_kernel<true>)
+                 : reinterpret_cast<const void*>(&dequant_t5_kernel<false>);
+  } else {
+    items = (size_t)N * (K / (32 / bits));
+    if (bits == 1)
+      fn = implied ? reinterpret_cast<const void*>(&dequant_words_kernel<1, true>)
+                   : reinterpret_cast<const void*>(&dequant_words_kernel<1, false>);
+    else
+      fn = implied ? reinterpret_cast<const void*>(&dequant_words_kernel<2, true>)
+                   : reinterpret_cast<const void*>(&dequant_words_kernel<2, false>);
+  }
+  const size_t blocks = (items + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return BQ_ERR_SHAPE;
+  return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+/*
+ * bq.h -- C ABI of the low-bit weight-quantized decode QMV library (gfx950).
+ *
+ * Source of the method: the web article "oMLX Bonsai 自定义内核: Qwen 系列快速
+ * QMV 路径完整解析" (cnnetsun.cn), section 二 (three kernel paths: qmv_fast,
+ * qmv_wide with its symmetric variant, the t5 ternary format with its qmv,
+ * qmv_wide and fused unpack+matmul qmm) and section 三 (an ABI probe guards
+ * the native extension).
+ *
+ * Shared conventions of every entry point
+ * ---------------------------------------
+ *   x       fp16 [M][K] row-major activations (device memory).
+ *   w       packed weights [N][row_bytes] (device memory), W[n][k] is the
+ *           weight from input k to output n:
+ *             bits = 1 or 2: uint32 words [N][K*bits/32]; code k of a row is
+ *             bits (k*bits)%32 .. +bits-1 of word (k*bits)/32 (LSB first).
+ *             bits = BQ_BITS_T5: uint8 [N][(K/gs)*ceil(gs/5)]; each group of
+ *             gs weights owns ceil(gs/5) bytes (13 for gs=64, 26 for 128);
+ *             code 5j+i of a group is base-3 digit i (least significant
+ *             first) of the group's byte j; unused digits are 0; a byte
+ *             above 242 is invalid (the result is then unspecified).
+ *   scales  fp16 [N][K/gs], one per (output row, group along K).
+ *   biases  fp16 [N][K/gs], or NULL where the call says so.  The weight is
+ *           w = scale*q + bias (group-wise affine quantization).
+ *   y       fp16 [M][N] row-major output, y[m][n] = sum_k x[m][k]*W[n][k],
+ *           accumulated in fp32 and rounded to fp16 (nearest even) once.
+ *           y is overwritten, never accumulated into.
+ *   M, N, K sizes; K must be a positive multiple of group_size; N > 0.
+ *   bits    1, 2, or BQ_BITS_T5 for the ternary format.
+ *   group_size  64 or 128.
+ *   stream  a hipStream_t (NULL = the default stream).  Every call only
+ *           enqueues work on it and returns; there is no synchronization.
+ *
+ * Ownership: all pointers are device pointers owned by the caller.  The
+ * library allocates nothing per call and keeps no mutable global state,
+ * so calls from several host threads are safe.
+ *
+ * Errors: each entry point validates every argument before it launches
+ * anything and returns BQ_OK (0) or a negative bq_status; bq_strerror()
+ * names it.  A failed launch returns BQ_ERR_HIP.  Nothing aborts or throws
+ * across this interface.
+ *
+ * Alignment: x, scales, biases and y need 2-byte alignment; w needs 4-byte
+ * alignment (uint32 words for bits 1/2; dword loads for t5).  The t5 entry
+ * points additionally need K to be a multiple of 256, so that every packed
+ * row is a whole number of dwords (true of all the decoder shapes).
+ */
+#ifndef BQ_H
+#define BQ_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQ_ABI_VERSION 1
+#define BQ_BITS_T5 0
+#define BQ_MAX_WIDE_M 5
+
+typedef enum bq_status {
+  BQ_OK = 0,
+  BQ_ERR_NULL = -1,       /* a required pointer is NULL */
+  BQ_ERR_BITS = -2,       /* bits not valid for this entry point */
+  BQ_ERR_GROUP = -3,      /* group_size not 64 or 128 */
+  BQ_ERR_SHAPE = -4,      /* N or K not positive, K % group_size != 0, or size overflow */
+  BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
+  BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
+  BQ_ERR_HIP = -7         /* the HIP runtime rejected a launch */
+} bq_status;
+
+/* ABI version of the loaded library; callers must refuse to use a library
+ * whose version differs from BQ_ABI_VERSION (the probe of section 三, but a
+ * mismatch is an error here, never a silent fallback). */
+int bq_abi_version(void);
+
+/* Static, NUL-terminated description of a bq_status value. */
+const char* bq_strerror(int status);
+
+/* qmv -- section 二 path 1 (qmv_fast): bits 1 or 2, biases required, any
+ * M >= 1.  Each activation row is an independent pass over W (W is read M
+ * times); row m gives the same bits as a call with M = 1 on that row. */
+int bq_qmv(const void* x, const void* w, const void* scales, const void* biases, void* y,
+           int M, int N, int K, int bits, int group_size, void* stream);
+
+/* qmv_wide -- section 二 path 2: bits 1 or 2, biases required,
+ * 1 <= M <= 5; one read of W serves all M rows.  Row m gives the same
+ * bits as bq_qmv on that row alone. */
+int bq_qmv_wide(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                int M, int N, int K, int bits, int group_size, void* stream);
+
+/* qmv_sym -- section 二 path 2, symmetric variant: bits 1 or 2,
+ * 1 <= M <= 5; the bias is implied as -scale*(2^bits-1)/2 and the biases
+ * argument is ignored and never read (it may be NULL).  Bit-identical to
+ * bq_qmv_wide with an explicit fp16 bias equal to -scale*(2^bits-1)/2
+ * whenever that value is exact in fp16. */
+int bq_qmv_sym(const void* x, const void* w, const void* scales, const void* biases, void* y,
+               int M, int N, int K, int bits, int group_size, void* stream);
+
+/* t5_qmv -- section 二 path 3: bits must be BQ_BITS_T5, any M >= 1 (each
+ * row an independent pass over W).  biases == NULL implies bias = -scale
+ * (weights in {-s, 0, +s}) and no bias is read; non-NULL biases are read. */
+int bq_t5_qmv(const void* x, const void* w, const void* scales, const void* biases, void* y,
+              int M, int N, int K, int bits, int group_size, void* stream);
+
+/* t5_qmv_wide -- section 二 path 3: as bq_t5_qmv with 1 <= M <= 5 and one
+ * read of W for all rows. */
+int bq_t5_qmv_wide(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                   int M, int N, int K, int bits, int group_size, void* stream);
+
+/* t5_qmm -- section 二 path 3 (prefill, M > 16 intended; any M >= 1):
+ * fused t5 unpack + matrix-core (MFMA, fp16 x fp16 -> fp32) product.  Each
+ * t5 byte is unpacked once per weight tile; biases as in bq_t5_qmv. */
+int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y,
+              int M, int N, int K, int bits, int group_size, void* stream);
+
+/* dequant -- section 二 path 1 (1-bit prefill dequantizes to float16
+ * before a matmul): y := fp16 [N][K], y[n][k] = fp16_rne(scale*q + bias)
+ * computed exactly and rounded once.  x is ignored (may be NULL) and so is
+ * M.  bits 1, 2 or BQ_BITS_T5.  biases == NULL implies -scale*(2^bits-1)/2
+ * for bits 1/2 and -scale for t5. */
+int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y,
+               int M, int N, int K, int bits, int group_size, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQ_H */

@@ -1,0 +1,164 @@
+"""The C ABI library loads and exports what include/bq.h declares, and every
+entry point rejects invalid arguments with its documented status before it
+touches the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_decode_qmv_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bq.h")
+
+OK, NULL, BITS, GROUP, SHAPE, MRANGE, ALIGN = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bq.LIB_PATH):
+        pytest.fail("libbq.so is not built: run __graft_entry__.build() first")
+    return bq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|int)\s+(bq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(bq.ALL_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 1
+
+
+def test_strerror_covers_every_status(lib):
+    msgs = {s: bq.strerror(s) for s in range(-7, 1)}
+    assert len(set(msgs.values())) == 8
+    assert bq.strerror(-99) == "unknown bq status"
+
+
+def test_abi_mismatch_is_an_error(tmp_path, monkeypatch):
+    monkeypatch.setattr(bq, "ABI_VERSION", 999)
+    with pytest.raises(ImportError, match="ABI version"):
+        bq.load_library(bq.LIB_PATH)
+
+
+def test_missing_library_is_an_error(tmp_path):
+    with pytest.raises(ImportError, match="not built"):
+        bq.load_library(str(tmp_path / "libbq.so"))
+
+
+# fake, aligned, never dereferenced device addresses: validation fails first
+P = 0x10000
+PX, PW, PS, PB, PY = P, 2 * P, 3 * P, 4 * P, 5 * P
+
+
+def call(lib, name, x=PX, w=PW, s=PS, b=PB, y=PY, M=1, N=8, K=256, bits=2, gs=64):
+    return getattr(lib, name)(x, w, s, b, y, M, N, K, bits, gs, None)
+
+
+U_ENTRIES = ["bq_qmv", "bq_qmv_wide", "bq_qmv_sym"]
+T5_ENTRIES = ["bq_t5_qmv", "bq_t5_qmv_wide", "bq_t5_qmm"]
+
+
+@pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES + ["bq_dequant"])
+def test_null_pointers(lib, name):
+    bits = 0 if name in T5_ENTRIES else 2
+    for kw in ("w", "s", "y"):
+        assert call(lib, name, bits=bits, **{kw: None}) == NULL
+    if name != "bq_dequant":
+        assert call(lib, name, bits=bits, x=None) == NULL
+
+
+@pytest.mark.parametrize("name", ["bq_qmv", "bq_qmv_wide"])
+def test_affine_entries_need_biases(lib, name):
+    assert call(lib, name, b=None) == NULL
+
+
+@pytest.mark.parametrize("name", U_ENTRIES)
+def test_bits_uint32_entries(lib, name):
+    for bits in (0, 3, 4, 8, -1):
+        assert call(lib, name, bits=bits) == BITS
+
+
+@pytest.mark.parametrize("name", T5_ENTRIES)
+def test_bits_t5_entries(lib, name):
+    for bits in (1, 2, 3):
+        assert call(lib, name, bits=bits) == BITS
+
+
+def test_bits_dequant(lib):
+    for bits in (3, 4, -1):
+        assert call(lib, "bq_dequant", bits=bits) == BITS
+
+
+@pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES + ["bq_dequant"])
+def test_group_size(lib, name):
+    bits = 0 if name in T5_ENTRIES else 2
+    for gs in (0, 32, 96, 256):
+        assert call(lib, name, bits=bits, gs=gs) == GROUP
+
+
+@pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES + ["bq_dequant"])
+def test_shapes(lib, name):
+    bits = 0 if name in T5_ENTRIES else 2
+    assert call(lib, name, bits=bits, N=0) == SHAPE
+    assert call(lib, name, bits=bits, N=-3) == SHAPE
+    assert call(lib, name, bits=bits, K=0) == SHAPE
+    assert call(lib, name, bits=bits, K=320, gs=128) == SHAPE
+    assert call(lib, name, bits=bits, K=(1 << 30) + 1024) == SHAPE
+
+
+@pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES)
+def test_m_range(lib, name):
+    bits = 0 if name in T5_ENTRIES else 2
+    assert call(lib, name, bits=bits, M=0) == MRANGE
+    assert call(lib, name, bits=bits, M=-1) == MRANGE
+    wide = name in ("bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv_wide")
+    assert (call(lib, name, bits=bits, M=6) == MRANGE) == wide
+
+
+@pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES + ["bq_dequant"])
+def test_alignment(lib, name):
+    bits = 0 if name in T5_ENTRIES else 2
+    assert call(lib, name, bits=bits, w=PW + 2) == ALIGN
+    assert call(lib, name, bits=bits, s=PS + 1) == ALIGN
+    assert call(lib, name, bits=bits, y=PY + 1) == ALIGN
+    if name != "bq_dequant":
+        assert call(lib, name, bits=bits, x=PX + 1) == ALIGN
+
+
+def test_t5_needs_k_multiple_of_256(lib):
+    for name in T5_ENTRIES:
+        assert call(lib, name, bits=0, K=192) == ALIGN
+        assert call(lib, name, bits=0, K=384, gs=128) == ALIGN
+    assert call(lib, "bq_dequant", bits=0, K=192) == ALIGN
+
+
+def test_qmm_and_dequant_vector_alignment(lib):
+    assert call(lib, "bq_t5_qmm", bits=0, x=PX + 8) == ALIGN
+    assert call(lib, "bq_dequant", bits=2, y=PY + 8) == ALIGN
+
+
+def test_binding_raises_with_status(lib):
+    with pytest.raises(bq.BQError) as ei:
+        bq.bq_qmv_wide(PX, PW, PS, PB, PY, 6, 8, 256, 2, 64)
+    assert ei.value.status == MRANGE and "BQ_ERR_M" in str(ei.value)
+
+
+def test_binding_tensor_helpers_refuse_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, dtype=torch.float16)
+    w = torch.zeros(1, 4, dtype=torch.int32)
+    s = torch.zeros(1, 1, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        bq.qmv_wide(x, w, s, s, 2, 64)
