@@ -36,6 +36,10 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   }
   if (gs != 64 && gs != 128) return BQ_ERR_GROUP;
   if (N <= 0 || K <= 0 || K % gs != 0 || K > (1 << 30)) return BQ_ERR_SHAPE;
+  // packed rows and scale rows are addressed with 32-bit offsets
+  if ((uint64_t)N * (uint64_t)row_bytes_of(bits == BQ_BITS_T5 ? BQ_BITS_T5 : 2, K, gs) >= (1ull << 30) ||
+      (uint64_t)N * (uint64_t)(K / gs) >= (1ull << 29))
+    return BQ_ERR_SHAPE;
   if (e != E_DEQUANT) {
     if (M < 1) return BQ_ERR_M;
     if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
@@ -44,7 +48,7 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if (x && !aligned(x, 2)) return BQ_ERR_ALIGN;
   if (!aligned(y, 2)) return BQ_ERR_ALIGN;
   if (bits == BQ_BITS_T5 && K % 256 != 0) return BQ_ERR_ALIGN;
-  if (e == E_QMM && !aligned(x, 16)) return BQ_ERR_ALIGN;
+  if (e != E_DEQUANT && !aligned(x, 16)) return BQ_ERR_ALIGN;
   if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
   return BQ_OK;
 }
@@ -56,20 +60,44 @@ int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, vo
 }
 
 // ---------------------------------------------------------------- qmv family
-// Rows per slot kept in registers, per M.
-template <int M> constexpr int rcap() { return M <= 2 ? 4 : (M <= 4 ? 3 : 2); }
+// Units kept in flight per slot (free to depend on M: it never changes the
+// arithmetic).
+template <int M> constexpr int ring_depth() { return 4; }
+constexpr int kSegTiles = 9;  // K tiles per x segment in LDS
+static_assert(kSegTiles * kKL * BQ_MAX_WIDE_M <= kStageRounds * kThreads, "x staging tasks per thread");
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMaxRowsPerWg = 256;
+constexpr size_t kLdsBudget = 150 * 1024;
+
+size_t qmv_lds_bytes(int M, int rows_per_wg, int ntiles, int seg_tiles) {
+  const size_t U = (size_t)((rows_per_wg + kR - 1) / kR) * ntiles;
+  const size_t cs = (size_t)M * kXD + ((M % 2 == 0) ? 4 : 0);
+  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL + U * kR * M);
+}
+
+// Workgroup geometry: a function of N and K only, never of M.
+void qmv_geometry(QmvParams& p) {
+  p.ntiles = (p.K + kTile - 1) / kTile;
+  p.seg_tiles = p.ntiles < kSegTiles ? p.ntiles : kSegTiles;
+  p.nseg = (p.ntiles + p.seg_tiles - 1) / p.seg_tiles;
+  int rows = kR * ((p.N + kR * kTargetWorkgroups - 1) / (kR * kTargetWorkgroups));
+  if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
+  while (rows > kR && qmv_lds_bytes(BQ_MAX_WIDE_M, rows, p.ntiles, p.seg_tiles) > kLdsBudget) rows -= kR;
+  p.rows_per_wg = rows;
+}
 
 template <int FMT, int GS, int M, bool IMPLIED>
 int launch_qmv_t(QmvParams p, void* stream) {
-  using F = Fmt<FMT, GS>;
-  constexpr int R = rcap<M>();
-  constexpr int SLOTS = kWaves * (64 / F::KL);
-  constexpr int TC = kTile / F::CH;
-  const size_t shmem = (size_t)(2 * M * TC * F::XD + 2 * M * TC) * sizeof(uint32_t);
-  p.rows_per_wg = SLOTS * R;
+  constexpr int P = ring_depth<M>();
+  qmv_geometry(p);
+  const size_t shmem = qmv_lds_bytes(M, p.rows_per_wg, p.ntiles, p.seg_tiles);
+  if (shmem > kLdsBudget) return BQ_ERR_SHAPE;
+  const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+  (void)attr;
   dim3 grid((p.N + p.rows_per_wg - 1) / p.rows_per_wg);
-  return launch(reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, R>), grid,
-                dim3(kThreads), shmem, stream, &p);
+  return launch(fn, grid, dim3(kThreads), shmem, stream, &p);
 }
 
 typedef int (*QmvLauncher)(QmvParams, void*);
@@ -116,10 +144,14 @@ int run_qmv(Entry e, const void* x, const void* w, const void* scales, const voi
   p.G = K / gs;
   p.row_bytes = row_bytes_of(bits, K, gs);
   p.ratio = t5 ? 1.0f : (bits == 1 ? 0.5f : 1.5f);
+  p.x_bytes = 0;  // per launch, below
+  p.w_bytes = (int)((size_t)N * p.row_bytes);
+  p.sb_bytes = (int)((size_t)N * p.G * 2);
   const bool per_row = (e == E_QMV || e == E_T5);
   const int rows_at_once = per_row ? 1 : M;
   QmvLauncher fn = pick_qmv(fmt, gs, rows_at_once, implied);
   if (!fn) return BQ_ERR_M;
+  p.x_bytes = rows_at_once * K * 2;
   for (int m0 = 0; m0 < M; m0 += rows_at_once) {
     p.x = static_cast<const half_t*>(x) + (size_t)m0 * K;
     p.y = static_cast<half_t*>(y) + (size_t)m0 * N;
@@ -143,7 +175,7 @@ const char* bq_strerror(int status) {
     case BQ_ERR_GROUP: return "group_size must be 64 or 128";
     case BQ_ERR_SHAPE: return "N and K must be positive, K a multiple of group_size and at most 2^30";
     case BQ_ERR_M: return "M is outside the range this entry point accepts";
-    case BQ_ERR_ALIGN: return "a pointer is misaligned, or a t5 call has K not a multiple of 256";
+    case BQ_ERR_ALIGN: return "a pointer is misaligned (x needs 16 bytes), or a t5 call has K not a multiple of 256";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown bq status";

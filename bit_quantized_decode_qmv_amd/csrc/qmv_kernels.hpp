@@ -10,34 +10,39 @@
 //
 // gfx950 design
 // -------------
-// * A workgroup is 4 waves.  A wave is split into slots of KL lanes (KL = 16,
-//   or 8 for t5 with 128-weight groups); the KL lanes of a slot share one
-//   output row and split its K range into chunks of CH codes (64, or 128),
-//   so one 1024-code K tile is one chunk per lane.  Each slot owns up to
-//   RCAP rows, which keeps x in registers across those rows.
-// * x is staged tile by tile in LDS (double buffered), permuted into the
-//   order in which the unpack below produces code pairs and pre-scaled per
-//   code position so that no shift is needed to line codes up (see
-//   "scaled codes").  Per-chunk sums of x feed the bias term.
-// * Scaled codes: a code masked in place inside a 16-bit half is read as an
-//   fp16 subnormal, i.e. q * 2^e * 2^-24 where e is its bit offset in the
-//   half.  v_dot2_f32_f16 multiplies it by the staged x*2^-e and adds in
-//   fp32, so every product is q*x*2^-24 exactly (up to the fp16 rounding of
-//   x*2^-e for |x| < 2^(e-14)); the 2^24 goes into the scale.  2-bit words
-//   need one shift per 16 codes, 1-bit words one per 32 codes.
-// * t5 bytes go through a 256-entry LDS table that turns a byte into its
-//   five base-3 digits laid out as 2-bit fields (digit i at bits 2i); two
-//   bytes fill one dword, and each mask then yields a half2 of codes.
-// * fp32 accumulation; per chunk: acc += b*X + (s*2^24)*P; a KL-lane
-//   butterfly reduces each row at the end and one lane stores fp16 (RNE).
-//
-// Every K chunk is always processed by the same lane in the same order and
-// the reduction tree does not depend on M, so row m of a wide call is
-// bit-identical to a call with that row alone.
+// * One workgroup of 8 waves per CU.  A wave holds four slots of 16 lanes;
+//   the 16 lanes of a slot cover one 1024-code K tile of R = 2 rows, each
+//   lane one chunk: 64 codes of 1/2-bit words (8 or 16 bytes) or one
+//   13-byte t5 run (a whole 64-group, or half of a 128-group: 65 + 63 codes).
+// * Work unit = (row-group of R rows, K tile).  The units of a workgroup,
+//   row-major, are cut into one contiguous range per slot; a slot keeps a
+//   ring of P units in flight, so HBM reads overlap the arithmetic without
+//   any barrier.  Consecutive units of one row-group accumulate in
+//   registers; each run is reduced over the slot's lanes into LDS, keyed by
+//   its first unit, and at the end every row adds its runs in unit order.
+//   The decomposition depends on N, K and the format only -- never on M --
+//   so row m of a wide call is bit-identical to a call with that row alone.
+// * x is staged per segment of K tiles in LDS, permuted into the order in
+//   which the unpack below produces code pairs and pre-scaled per code
+//   position.  Its loads are issued before the ring loads so that waiting
+//   for x never waits for W.
+// * Scaled codes: a code masked in place inside a 16-bit half reads as the
+//   fp16 subnormal q * 2^e * 2^-24, e its bit offset in the half;
+//   v_dot2_f32_f16 multiplies it by the staged x*2^-e, so every product is
+//   q*x*2^-24 exactly (up to the fp16 rounding of x*2^-e when
+//   |x| < 2^(e-14)), with no per-code conversion; 2^24 goes into the scale.
+// * t5 bytes go through a 256-entry LDS table that holds a byte's five
+//   base-3 digits as 2-bit fields; two bytes fill one dword and five masks
+//   give five half2 code pairs.  13-byte runs are loaded as one dword-aligned
+//   16-byte window and realigned with v_alignbyte_b32.
+// * Epilogue per chunk: acc = fma(s*2^24, P, fma(b, X, acc)) in fp32 with X
+//   the chunk's (or, for 128-groups, the group's) sum of x.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace bq {
 
@@ -45,15 +50,17 @@ typedef _Float16 half_t;
 typedef half_t half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-// dword-aligned (not 16-byte aligned) views for t5 rows
+// dword-aligned (not 16-byte aligned) view for t5 rows
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
 
 enum { FMT_U1 = 1, FMT_U2 = 2, FMT_T5 = 5 };
-constexpr int kTile = 1024;       // codes per K tile
-constexpr int kWaves = 4;         // waves per workgroup
+constexpr int kTile = 1024;        // codes per K tile
+constexpr int kKL = 16;            // lanes per slot (chunks per tile)
+constexpr int kWaves = 8;          // waves per workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kSlots = kThreads / kKL;
+constexpr int kR = 2;              // rows per row-group
+constexpr int kXD = 36;            // LDS dwords per staged chunk (32-35 used)
 
 struct QmvParams {
   const half_t* x;       // [M][K]
@@ -63,76 +70,82 @@ struct QmvParams {
   half_t* y;             // [M][N]
   int N, K, G;           // G = K / group_size
   int row_bytes;
-  int rows_per_wg;       // rows of one workgroup (<= slots * RCAP)
+  int rows_per_wg;       // rows of one workgroup
+  int ntiles;            // ceil(K / kTile)
+  int seg_tiles;         // tiles per x segment staged in LDS
+  int nseg;              // ceil(ntiles / seg_tiles)
+  int x_bytes;           // M * K * 2 (buffer descriptor size)
+  int w_bytes;           // N * row_bytes (buffer descriptor size)
+  int sb_bytes;          // N * G * 2
   float ratio;           // implied bias = -scale * ratio
 };
 
 // --------------------------------------------------------------------------
-// Format traits
-//   CH  codes per chunk (one lane, one row, one K tile)
-//   KL  lanes per slot  (KL * CH = kTile)
-//   XD  LDS dwords per staged chunk (padded so that the 16 chunks of a tile
-//       start on distinct banks)
-//   place(pos) -> staged dword, half and exponent of chunk position pos
+// Format traits.  place(pos) maps code `pos` of a K tile (0..1023) to its
+// chunk, staged dword, half and exponent; CB = packed bytes per chunk.
 // --------------------------------------------------------------------------
 template <int FMT, int GS> struct Fmt;
 
+// 2-bit: word i of a chunk holds codes 16i..16i+15; pair p = (code p, code
+// p+8); pairs 0..4 are masked in place (offset 2p), pairs 5..7 after >> 10.
 template <int GS> struct Fmt<FMT_U2, GS> {
-  static constexpr int CH = 64, KL = 16, XD = 36, XUSED = 32;
-  // word i holds codes 16i..16i+15; pair p = (code p, code p+8) of a word;
-  // pairs 0..4 are masked in place (offset 2p), pairs 5..7 after >> 10.
-  __device__ static inline void place(int pos, int& d, int& h, int& e) {
-    int i = pos >> 4, j = pos & 15, pp = j & 7;
+  static constexpr int CB = 16;
+  __device__ static inline void place(int pos, int& c, int& d, int& h, int& e) {
+    c = pos >> 6;
+    const int q = pos & 63, i = q >> 4, j = q & 15, pp = j & 7;
     h = j >> 3;
     d = 8 * i + pp;
     e = 2 * (pp < 5 ? pp : pp - 5);
   }
 };
 
+// 1-bit: word i of a chunk holds codes 32i..32i+31; pair p = (code p,
+// code p+16); pairs 0..9 masked in place (offset p), 10..15 after >> 10.
 template <int GS> struct Fmt<FMT_U1, GS> {
-  static constexpr int CH = 64, KL = 16, XD = 36, XUSED = 32;
-  // word i holds codes 32i..32i+31; pair p = (code p, code p+16);
-  // pairs 0..9 masked in place (offset p), pairs 10..15 after >> 10.
-  __device__ static inline void place(int pos, int& d, int& h, int& e) {
-    int i = pos >> 5, j = pos & 31, pp = j & 15;
+  static constexpr int CB = 8;
+  __device__ static inline void place(int pos, int& c, int& d, int& h, int& e) {
+    c = pos >> 6;
+    const int q = pos & 63, i = q >> 5, j = q & 31, pp = j & 15;
     h = j >> 4;
     d = 16 * i + pp;
     e = pp < 10 ? pp : pp - 10;
   }
 };
 
-// t5: byte t of a chunk holds codes 5t..5t+4.  Bytes (2p, 2p+1) form pair p;
-// digit i (i < 4) of pair p is staged at dword 4p+i, digit 4 at NP4 + p.
+// t5: a chunk is 13 bytes; bytes (2p, 2p+1), p < 6, form pair p whose digit
+// i < 4 is staged at dword 4p+i and digit 4 at 28+p; byte 12 is single: its
+// digits 0..3 at dwords 24..27 and digit 4 at dword 34.
+__device__ inline void t5_slot(int t, int i, int& d, int& h) {
+  if (t < 12) {
+    const int p = t >> 1;
+    h = t & 1;
+    d = (i < 4) ? 4 * p + i : 28 + p;
+  } else {
+    h = 0;
+    d = (i < 4) ? 24 + i : 34;
+  }
+}
+
 template <> struct Fmt<FMT_T5, 64> {
-  static constexpr int CH = 64, KL = 16, XD = 36, XUSED = 34;
-  static constexpr int NPAIR = 6;       // bytes 0..11; byte 12 is single
-  static constexpr int NP4 = 28;        // first dword of the digit-4 block
-  static constexpr int BYTES = 13;
-  __device__ static inline void place(int pos, int& d, int& h, int& e) {
-    int t = pos / 5, i = pos - 5 * (pos / 5);
+  static constexpr int CB = 13;
+  __device__ static inline void place(int pos, int& c, int& d, int& h, int& e) {
+    c = pos >> 6;
+    const int q = pos & 63, t = q / 5, i = q - 5 * t;
     e = 2 * i;
-    if (t < 12) {
-      int p = t >> 1;
-      h = t & 1;
-      d = (i < 4) ? 4 * p + i : NP4 + p;
-    } else {              // byte 12: codes 60..63 (+ one zero pad digit)
-      h = 0;
-      d = 24 + i;
-    }
+    t5_slot(t, i, d, h);
   }
 };
 
+// 128-groups are split into bytes 0..12 (codes 0..64) and bytes 13..25
+// (codes 65..127 and two zero pad digits): chunks 2g and 2g+1.
 template <> struct Fmt<FMT_T5, 128> {
-  static constexpr int CH = 128, KL = 8, XD = 68, XUSED = 65;
-  static constexpr int NPAIR = 13;      // bytes 0..25 (byte 25: 3 digits + 2 pads)
-  static constexpr int NP4 = 52;
-  static constexpr int BYTES = 26;
-  __device__ static inline void place(int pos, int& d, int& h, int& e) {
-    int t = pos / 5, i = pos - 5 * (pos / 5);
-    int p = t >> 1;
+  static constexpr int CB = 13;
+  __device__ static inline void place(int pos, int& c, int& d, int& h, int& e) {
+    const int g = pos >> 7, r = pos & 127, hi = r >= 65 ? 1 : 0;
+    c = 2 * g + hi;
+    const int byte = r / 5, i = r - 5 * byte;
     e = 2 * i;
-    h = t & 1;
-    d = (i < 4) ? 4 * p + i : NP4 + p;
+    t5_slot(byte - 13 * hi, i, d, h);
   }
 };
 
@@ -145,12 +158,64 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ float h2f(half_t v) { return (float)v; }
+__device__ __forceinline__ float lo_half(uint32_t v) {
+  return h2f(__builtin_bit_cast(half_t, (uint16_t)(v & 0xFFFFu)));
+}
+__device__ __forceinline__ float hi_half(uint32_t v) {
+  return h2f(__builtin_bit_cast(half_t, (uint16_t)(v >> 16)));
+}
 
-template <int W>
-__device__ __forceinline__ float lane_sum(float v) {
+// Sum over the 16 lanes of a DPP row (row_shr 1, 2, 4, 8 with zero fill):
+// the last lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float v) {
+  int x = __builtin_bit_cast(int, v);
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false)));
+  x = __builtin_bit_cast(int, __builtin_bit_cast(float, x) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false)));
+  return __builtin_bit_cast(float, x);
+}
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
+// global memory, which on this GPU waits for every load in flight (loads and
+// stores share one counter) and would drain the prefetched weights; here only
+// the LDS traffic is waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Forces the partial sums to be computed here: keeps the compiler from
+// sinking the dot products of several quads below later loads, which would
+// keep a whole chunk of x live in registers.
+template <int M>
+__device__ __forceinline__ void pin_partials(float (&Pd)[kR][M]) {
 #pragma unroll
-  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) asm volatile("" : "+v"(Pd[r][m]));
+}
+
+// Half `h` of dword a next to half `g` of dword b: (a.h, b.g) as one dword.
+__device__ __forceinline__ uint32_t pair_halves(uint32_t a, int h, uint32_t b, int g) {
+  const uint32_t lo = h ? (a >> 16) : (a & 0xFFFFu);
+  const uint32_t hi = g ? (b & 0xFFFF0000u) : (b << 16);
+  return lo | hi;
+}
+
+// (lo, hi) fp16 pair times 2^-e (exact unless the result is subnormal, then
+// rounded to nearest even, as one fp16 rounding of x*2^-e).
+__device__ __forceinline__ uint32_t scale_pair(uint32_t v, int e) {
+  const half2_t f = __builtin_bit_cast(half2_t, v);
+  const half_t sc = (half_t)__builtin_ldexpf(1.0f, -e);
+  const half2_t r = f * half2_t{sc, sc};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // t5 digit table entry: digit i of byte v at bits 2i..2i+1.
@@ -164,327 +229,484 @@ __device__ __forceinline__ uint32_t t5_fields(uint32_t v) {
   return f;
 }
 
-// Per-lane packed chunk of one row.
-template <int FMT, int GS> struct Chunk;
-template <int GS> struct Chunk<FMT_U2, GS> { u32x4 v; };
-template <int GS> struct Chunk<FMT_U1, GS> { u32x2 v; };
-template <> struct Chunk<FMT_T5, 64> { uint32_t d[4]; };
-template <> struct Chunk<FMT_T5, 128> { uint32_t d[7]; };
+// LDS dwords per staged chunk for all M rows: M*kXD, padded so that the 16
+// chunks of a tile start on distinct 4-dword bank groups.
+template <int M> constexpr int chunk_stride() { return M * kXD + ((M % 2 == 0) ? 4 : 0); }
 
-template <int FMT, int GS>
-__device__ __forceinline__ void load_chunk(Chunk<FMT, GS>& c, const uint8_t* w, int row, int chunk,
-                                           int row_bytes) {
-  const uint8_t* rp = w + (size_t)row * row_bytes;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int bytes) {
+  // dword 3 of a raw buffer descriptor on gfx9-class GPUs; reads outside
+  // [0, bytes) return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Packed chunk of one row held by one lane.
+template <int FMT> struct Chunk;
+template <> struct Chunk<FMT_U2> { u32x4 v; };
+template <> struct Chunk<FMT_U1> { u32x2 v; };
+template <> struct Chunk<FMT_T5> { u32x4 v; };
+
+// `off` (per lane) + `soff` (uniform) bytes into the packed rows.
+template <int FMT>
+__device__ __forceinline__ void load_chunk(Chunk<FMT>& c, rsrc_t w, uint32_t off, int soff) {
   if constexpr (FMT == FMT_U2) {
-    c.v = *reinterpret_cast<const u32x4*>(rp + chunk * 16);
+    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)off, soff, 0);
   } else if constexpr (FMT == FMT_U1) {
-    c.v = *reinterpret_cast<const u32x2*>(rp + chunk * 8);
-  } else if constexpr (GS == 64) {
-    // 13 bytes at rp + 13*chunk; rows are whole dwords, so the dword-aligned
-    // 16-byte window that holds them never passes the end of the row.
-    int off = 13 * chunk;
-    const u32x4 v = *reinterpret_cast<const u32x4a*>(rp + (off & ~3));
-    c.d[0] = v[0]; c.d[1] = v[1]; c.d[2] = v[2]; c.d[3] = v[3];
+    c.v = __builtin_amdgcn_raw_buffer_load_b64(w, (int)off, soff, 0);
   } else {
-    // 26 bytes at rp + 26*chunk, dword offset 0 or 2: seven dwords hold them.
-    int off = 26 * chunk;
-    const uint8_t* p = rp + (off & ~3);
-    const u32x4 a = *reinterpret_cast<const u32x4a*>(p);
-    const u32x3 b = *reinterpret_cast<const u32x3a*>(p + 16);
-    c.d[0] = a[0]; c.d[1] = a[1]; c.d[2] = a[2]; c.d[3] = a[3];
-    c.d[4] = b[0]; c.d[5] = b[1]; c.d[6] = b[2];
+    // 13 bytes at off + soff; rows are whole dwords (soff a multiple of 4),
+    // so the dword-aligned 16-byte window that holds them never passes the
+    // end of the row.
+    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)(off & ~3u), soff, 0);
   }
 }
 
 // --------------------------------------------------------------------------
-// Staging of one K tile of x into LDS, plus per-chunk sums of x.
-// Thread t stages codes 4t..4t+3 of the tile for every row m.
+// x staging of one segment (Ts tiles from tile s0).  Task = (m, tile,
+// chunk): one thread loads the chunk's 64 x values (65/63 for the halves of
+// a t5 128-group), writes its staged dwords (permuted into the order the
+// unpack produces code pairs, pre-scaled by 2^-e) with 16-byte LDS stores
+// and its sum of x.  xstage_issue loads into registers, xstage_commit
+// writes LDS, so that other loads can be issued in between.
 // --------------------------------------------------------------------------
+template <int FMT, int GS> struct XSpan {
+  // x dwords a task loads (as 16-byte vectors) and the code offset of the
+  // first one relative to the chunk's nominal start 64*c
+  static constexpr int VEC = (FMT == FMT_T5 && GS == 128) ? 9 : 8;
+};
+
+template <int FMT, int GS> struct XStage { u32x4 v[XSpan<FMT, GS>::VEC]; int task; };
+constexpr int kStageRounds = 2;  // staging tasks per thread
+
 template <int FMT, int GS, int M>
-__device__ __forceinline__ void stage_tile(const QmvParams& p, int tile, uint32_t* xs, float* xsum) {
-  using F = Fmt<FMT, GS>;
-  constexpr int TC = kTile / F::CH;
-  const int tid = threadIdx.x;
-  const int k0 = tile * kTile + 4 * tid;
-  uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
+__device__ __forceinline__ void xstage_issue(const QmvParams& p, rsrc_t rx, int s0, int Ts, int task,
+                                             XStage<FMT, GS>& st) {
+  constexpr int VEC = XSpan<FMT, GS>::VEC;
+  st.task = task;
+  const int c = task % kKL, tt = (task / kKL) % Ts, m = min(task / (kKL * Ts), M);
+  // the chunk's nominal first code; t5 128-groups: chunk 2g loads from code
+  // 128g, chunk 2g+1 from 128g+64 (both 16-byte aligned).  Loads are always
+  // issued; a task past M reads past the end of x (zeros), unused anyway.
+  const uint32_t off = 2u * ((uint32_t)m * (uint32_t)p.K + (uint32_t)((s0 + tt) * kTile + 64 * c));
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float part = 0.f;
-    if (k0 < p.K) {
-      const half_t* xr = p.x + (size_t)m * p.K + k0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        half_t v = xr[u];
-        float f = h2f(v);
-        part += f;
-        int pos = (4 * tid + u) % F::CH;
-        int c = (4 * tid + u) / F::CH;
-        int d, h, e;
-        F::place(pos, d, h, e);
-        half_t sv = (half_t)__builtin_ldexpf(f, -e);
-        xs16[2 * ((m * TC + c) * F::XD + d) + h] = __builtin_bit_cast(uint16_t, sv);
-      }
-    }
-    part = lane_sum<F::CH / 4>(part);
-    if ((tid % (F::CH / 4)) == 0) xsum[m * TC + (4 * tid) / F::CH] = part;
-  }
+  for (int j = 0; j < VEC; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16u * j), 0, 0);
 }
 
-// --------------------------------------------------------------------------
-// Per-chunk multiply: P[r][m] += codes(row r) . xstaged(m), for all rows of
-// the slot that are active.
-// --------------------------------------------------------------------------
-template <int FMT, int GS, int M, int RCAP>
-__device__ __forceinline__ void chunk_dot(const Chunk<FMT, GS> (&wc)[RCAP], const uint32_t* xc,
-                                          int xstride_m, const uint16_t* lut, int nrows,
-                                          uint32_t sh, float (&P)[RCAP][M]) {
-  using F = Fmt<FMT, GS>;
+template <int FMT, int GS, int M>
+__device__ __forceinline__ void xstage_commit(const QmvParams& p, int s0, int Ts, const XStage<FMT, GS>& st,
+                                              uint32_t* xs, float* xsum) {
+  const int task = st.task;
+  if (task >= M * Ts * kKL) return;  // whole waves without a task skip the work
+  const int c = task % kKL, tt = (task / kKL) % Ts, m = task / (kKL * Ts);
+  const int k0 = (s0 + tt) * kTile + 64 * c;
+  const bool live = k0 < p.K;
+  // X[j] = (x[2j], x[2j+1]) of the loaded span
+  auto X = [&](int j) -> uint32_t { return st.v[j >> 2][j & 3]; };
+  auto H = [&](int k) -> uint32_t { return (X(k >> 1) >> (16 * (k & 1))) & 0xFFFFu; };  // x[k] bits
+  auto P2 = [&](int k0_, int k1_, int e) -> uint32_t {  // (x[k0], x[k1]) * 2^-e; k < 0 means 0
+    const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
+    const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
+    return scale_pair(lo | (hi << 16), e);
+  };
+  uint32_t out[36];
+#pragma unroll
+  for (int d = 0; d < 36; ++d) out[d] = 0u;
+  float sum = 0.f;
+  const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0)
   if constexpr (FMT == FMT_U2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 xa[M], xb[M];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        xa[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + 8 * i);
-        xb[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + 8 * i + 4);
+      for (int pp = 0; pp < 8; ++pp) {
+        const int e = 2 * (pp < 5 ? pp : pp - 5);
+        out[8 * i + pp] = P2(16 * i + pp, 16 * i + pp + 8, e);
       }
 #pragma unroll
-      for (int r = 0; r < RCAP; ++r) {
-        if (r < nrows) {
-          uint32_t wv = wc[r].v[i];
-          uint32_t ws = wv >> 10;
-          uint32_t q[8];
+    for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
+  } else if constexpr (FMT == FMT_U1) {
 #pragma unroll
-          for (int pp = 0; pp < 5; ++pp) q[pp] = wv & (0x00030003u << (2 * pp));
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int pp = 5; pp < 8; ++pp) q[pp] = ws & (0x00030003u << (2 * (pp - 5)));
+      for (int pp = 0; pp < 16; ++pp) {
+        const int e = pp < 10 ? pp : pp - 10;
+        out[16 * i + pp] = P2(32 * i + pp, 32 * i + pp + 16, e);
+      }
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float a = P[r][m];
-            a = dot2(q[0], xa[m][0], a);
-            a = dot2(q[1], xa[m][1], a);
-            a = dot2(q[2], xa[m][2], a);
-            a = dot2(q[3], xa[m][3], a);
-            a = dot2(q[4], xb[m][0], a);
-            a = dot2(q[5], xb[m][1], a);
-            a = dot2(q[6], xb[m][2], a);
-            a = dot2(q[7], xb[m][3], a);
-            P[r][m] = a;
+    for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
+  } else if constexpr (GS == 64) {
+    // codes 0..63: pairs p < 6 hold codes 10p+i / 10p+5+i; byte 12 codes 60..63
+#pragma unroll
+    for (int pr = 0; pr < 6; ++pr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * pr + i] = P2(10 * pr + i, 10 * pr + 5 + i, 2 * i);
+      out[28 + pr] = P2(10 * pr + 4, 10 * pr + 9, 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[24 + i] = P2(60 + i, -1, 2 * i);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
+  } else {
+    // 128-group halves.  Even chunk: codes 0..64 of the group, loaded from
+    // the group start.  Odd chunk: codes 65..127, loaded from code 64 of the
+    // group (the chunk's nominal start), so local code q sits at span q+1.
+    auto half_group = [&](auto HI) {
+      constexpr int off = decltype(HI)::value;  // span index of local code 0
+#pragma unroll
+      for (int pr = 0; pr < 6; ++pr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[4 * pr + i] = P2(off + 10 * pr + i, off + 10 * pr + 5 + i, 2 * i);
+        out[28 + pr] = P2(off + 10 * pr + 4, off + 10 * pr + 9, 8);
+      }
+      // single byte: even chunk byte 12 = codes 60..64 (5 digits); odd chunk
+      // byte 25 = codes 125..127 (3 digits) = local 60..62
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[24 + i] = P2((off == 1 && i == 3) ? -1 : off + 60 + i, -1, 2 * i);
+      out[34] = P2(off == 1 ? -1 : 64, -1, 8);
+      // sum of this half's codes: even 0..64 (span 0..64), odd 65..127 (span 1..63)
+      if constexpr (off == 0) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
+        sum += h2f(__builtin_bit_cast(half_t, (uint16_t)H(64)));
+      } else {
+        sum = h2f(__builtin_bit_cast(half_t, (uint16_t)(X(0) >> 16)));
+#pragma unroll
+        for (int j = 1; j < 32; ++j) sum = dot2(X(j), ones, sum);
+      }
+    };
+    if (c & 1) half_group(std::integral_constant<int, 1>{});
+    else half_group(std::integral_constant<int, 0>{});
+  }
+  if constexpr (FMT == FMT_T5 && GS == 128) {
+    // the group's sum goes to its even chunk; odd chunks carry 0
+    const float other = __shfl_xor(sum, 1, 64);
+    sum = (c & 1) ? 0.f : sum + other;
+  }
+  if (live) {
+    uint32_t* dst = xs + (tt * kKL + c) * chunk_stride<M>() + m * kXD;
+#pragma unroll
+    for (int q = 0; q < 9; ++q)
+      *reinterpret_cast<u32x4*>(dst + 4 * q) = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+    xsum[(tt * kKL + c) * M + m] = sum * 5.9604644775390625e-08f;  // * 2^-24, like the products
+  }
+}
+
+// --------------------------------------------------------------------------
+// Per-chunk multiply: Pd[r][m] = codes(row r) . xstaged(m).
+// xc points at the lane's staged chunk; row m of x is kXD dwords further.
+// --------------------------------------------------------------------------
+template <int FMT, int M>
+__device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint32_t* xc,
+                                          const uint16_t* lut, uint32_t sh, float (&Pd)[kR][M]) {
+  if constexpr (FMT == FMT_U2 || FMT == FMT_U1) {
+    // quad q = 4 staged dwords 4q..4q+3 (2-bit: word q/2, pairs 4(q%2)..;
+    // 1-bit: word q/4, pairs 4(q%4)..); the next quad's x is read while
+    // this one is multiplied
+    u32x4 xb[2][M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xb[0][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q + 1 < 8) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) xb[(q + 1) & 1][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD + 4 * (q + 1));
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        uint32_t c4[4];
+        if constexpr (FMT == FMT_U2) {
+          const uint32_t wv = wc[r].v[q >> 1];
+          if ((q & 1) == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) c4[u] = wv & (0x00030003u << (2 * u));
+          } else {
+            const uint32_t ws = wv >> 10;
+            c4[0] = wv & 0x03000300u;
+            c4[1] = ws & 0x00030003u;
+            c4[2] = ws & 0x000C000Cu;
+            c4[3] = ws & 0x00300030u;
+          }
+        } else {
+          const uint32_t wv = wc[r].v[q >> 2];
+          const uint32_t ws = wv >> 10;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int pp = 4 * (q & 3) + u;
+            c4[u] = pp < 10 ? (wv & (0x00010001u << pp)) : (ws & (0x00010001u << (pp - 10)));
           }
         }
-      }
-    }
-  } else if constexpr (FMT == FMT_U1) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {  // pairs 8*half .. 8*half+7
-        u32x4 xa[M], xb[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          xa[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + 16 * i + 8 * half);
-          xb[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + 16 * i + 8 * half + 4);
-        }
-#pragma unroll
-        for (int r = 0; r < RCAP; ++r) {
-          if (r < nrows) {
-            uint32_t wv = wc[r].v[i];
-            uint32_t ws = wv >> 10;
-            uint32_t q[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              int pp = 8 * half + u;
-              q[u] = pp < 10 ? (wv & (0x00010001u << pp)) : (ws & (0x00010001u << (pp - 10)));
-            }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              float a = P[r][m];
-              a = dot2(q[0], xa[m][0], a);
-              a = dot2(q[1], xa[m][1], a);
-              a = dot2(q[2], xa[m][2], a);
-              a = dot2(q[3], xa[m][3], a);
-              a = dot2(q[4], xb[m][0], a);
-              a = dot2(q[5], xb[m][1], a);
-              a = dot2(q[6], xb[m][2], a);
-              a = dot2(q[7], xb[m][3], a);
-              P[r][m] = a;
-            }
-          }
+          float acc = Pd[r][m];
+          acc = dot2(c4[0], xb[q & 1][m][0], acc);
+          acc = dot2(c4[1], xb[q & 1][m][1], acc);
+          acc = dot2(c4[2], xb[q & 1][m][2], acc);
+          acc = dot2(c4[3], xb[q & 1][m][3], acc);
+          Pd[r][m] = acc;
         }
       }
+      pin_partials<M>(Pd);
     }
   } else {
-    // t5: realign each row's bytes (the chunk starts at byte offset `sh`
-    // of its first dword), then look pairs of bytes up in the digit table.
-    constexpr int NDW = (GS == 64) ? 4 : 7;
-    constexpr int NP = F::NPAIR + ((GS == 64) ? 1 : 0);  // + single byte 12
-    uint32_t rb[RCAP][NDW];
+    // t5: realign each row's 13 bytes (they start `sh` bytes into the first
+    // dword), then six byte pairs and the single byte 12 via the table
+    uint32_t rb[kR][4];
 #pragma unroll
-    for (int r = 0; r < RCAP; ++r) {
+    for (int r = 0; r < kR; ++r) {
 #pragma unroll
-      for (int j = 0; j < NDW; ++j) {
-        const uint32_t lo = wc[r].d[j];
-        const uint32_t hi = (j + 1 < NDW) ? wc[r].d[j + 1] : 0u;
-        rb[r][j] = __builtin_amdgcn_alignbyte(hi, lo, sh);
-      }
+      for (int j = 0; j < 4; ++j)
+        rb[r][j] = __builtin_amdgcn_alignbyte(j < 3 ? wc[r].v[j + 1] : 0u, wc[r].v[j], sh);
+    }
+    u32x4 xq[2][M];
+    uint32_t x4[2][M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      xq[0][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD);
+      x4[0][m] = xc[m * kXD + 28];
     }
 #pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-      const bool paired = pr < F::NPAIR;
-      u32x4 xq[M], x4[M];
+    for (int pr = 0; pr < 7; ++pr) {
+      const bool paired = pr < 6;
+      if (pr + 1 < 7) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        xq[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + 4 * pr);
-        if (paired) x4[m] = *reinterpret_cast<const u32x4*>(xc + m * xstride_m + F::NP4 + 4 * (pr / 4));
-      }
-#pragma unroll
-      for (int r = 0; r < RCAP; ++r) {
-        if (r < nrows) {
-          const int t0 = 2 * pr, t1 = 2 * pr + 1;
-          uint32_t b0 = (rb[r][t0 >> 2] >> (8 * (t0 & 3))) & 0xFFu;
-          uint32_t v = lut[b0];
-          if (paired) {
-            uint32_t b1 = (rb[r][t1 >> 2] >> (8 * (t1 & 3))) & 0xFFu;
-            v |= (uint32_t)lut[b1] << 16;
-          }
-          uint32_t q0 = v & 0x00030003u, q1 = v & 0x000C000Cu, q2 = v & 0x00300030u,
-                   q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float a = P[r][m];
-            a = dot2(q0, xq[m][0], a);
-            a = dot2(q1, xq[m][1], a);
-            a = dot2(q2, xq[m][2], a);
-            a = dot2(q3, xq[m][3], a);
-            if (paired) a = dot2(q4, x4[m][pr & 3], a);
-            P[r][m] = a;
-          }
+        for (int m = 0; m < M; ++m) {
+          xq[(pr + 1) & 1][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD + 4 * (pr + 1));
+          x4[(pr + 1) & 1][m] = xc[m * kXD + (pr + 1 < 6 ? 28 + pr + 1 : 34)];
         }
       }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int t0 = 2 * pr, t1 = 2 * pr + 1;
+        const uint32_t b0 = (rb[r][t0 >> 2] >> (8 * (t0 & 3))) & 0xFFu;
+        uint32_t v = lut[b0];
+        if (paired) {
+          const uint32_t b1 = (rb[r][t1 >> 2] >> (8 * (t1 & 3))) & 0xFFu;
+          v |= (uint32_t)lut[b1] << 16;
+        }
+        const uint32_t q0 = v & 0x00030003u, q1 = v & 0x000C000Cu, q2 = v & 0x00300030u,
+                       q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float acc = Pd[r][m];
+          acc = dot2(q0, xq[pr & 1][m][0], acc);
+          acc = dot2(q1, xq[pr & 1][m][1], acc);
+          acc = dot2(q2, xq[pr & 1][m][2], acc);
+          acc = dot2(q3, xq[pr & 1][m][3], acc);
+          acc = dot2(q4, x4[pr & 1][m], acc);
+          Pd[r][m] = acc;
+        }
+      }
+      pin_partials<M>(Pd);
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// The kernel.  Workgroup g owns rows [g*rows_per_wg, ...); slot s of the
-// workgroup owns rows base + s + j*SLOTS (j < RCAP).
+// The kernel.
 // --------------------------------------------------------------------------
-template <int FMT, int GS, int M, bool IMPLIED, int RCAP>
+template <int FMT, int GS, int M, bool IMPLIED, int P>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   using F = Fmt<FMT, GS>;
-  constexpr int TC = kTile / F::CH;              // chunks per tile (= KL)
-  constexpr int WSLOTS = 64 / F::KL;             // slots per wave
-  constexpr int SLOTS = kWaves * WSLOTS;         // slots per workgroup
-  constexpr int XT = M * TC * F::XD;             // dwords of one staged tile
-  constexpr bool T5 = (FMT == FMT_T5);
-
+  constexpr int CS = chunk_stride<M>();
   extern __shared__ uint32_t smem[];
-  uint32_t* xs = smem;                           // [2][XT]
-  float* xsum = reinterpret_cast<float*>(smem + 2 * XT);  // [2][M*TC]
   __shared__ uint16_t lut[256];
 
+  const int ST = p.seg_tiles;
+  const int T = p.ntiles;
+  uint32_t* xs = smem;                                             // [ST*16][CS]
+  float* xsum = reinterpret_cast<float*>(smem + ST * kKL * CS);    // [ST*16][M]
+  float* part = xsum + ST * kKL * M;                               // [U][kR*M]
+
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int slot = (tid >> 6) * WSLOTS + lane / F::KL;
-  const int kl = lane % F::KL;
+  const int slot = tid / kKL;
+  const int kl = tid % kKL;
   const int base = blockIdx.x * p.rows_per_wg;
-  const int end = min(base + p.rows_per_wg, p.N);
-  int nrows = 0;
+  const int nrow_wg = min(p.rows_per_wg, p.N - base);
+  const int G = (nrow_wg + kR - 1) / kR;
+  const int nchunks = p.K / 64;
+  const uint32_t sh = (uint32_t)(kl & 3);  // t5 run offset inside its first dword
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.sb_bytes);
+  const rsrc_t rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+
+  // x of segment 0 first, so that waiting for it never waits for W
+  XStage<FMT, GS> xst[kStageRounds];
 #pragma unroll
-  for (int r = 0; r < RCAP; ++r)
-    if (base + slot + r * SLOTS < end) nrows = r + 1;
+  for (int k = 0; k < kStageRounds; ++k) xstage_issue<FMT, GS, M>(p, rx, 0, min(ST, T), tid + k * kThreads, xst[k]);
 
-  for (int i = tid; i < 2 * XT; i += kThreads) xs[i] = 0u;  // pads stay zero
-  if constexpr (T5) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
+  for (int i = tid; i < ST * kKL * CS; i += kThreads) xs[i] = 0u;
+  if constexpr (FMT == FMT_T5) {
+    if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
+  }
 
-  const int nchunks = p.K / F::CH;
-  const int ntiles = (p.K + kTile - 1) / kTile;
-  // byte offset of this lane's t5 chunk inside its first dword
-  const uint32_t sh = (GS == 64) ? (uint32_t)(kl & 3) : (uint32_t)((2 * kl) & 3);
+  auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
+  // slot k's units of segment s: [lo(k), lo(k+1)) with lo(k) = k*U_s/kSlots
+  auto range_lo_of = [&](int k, int Us) { return (k * Us) / kSlots; };
 
-  float acc[RCAP][M];
+  // ---- fetch cursor: unit (row-group, tile ft) of the current segment.
+  // Every unit issues the same loads (rows past N and chunks past K read
+  // zeros or data that is never used), so the compiler can wait for exactly
+  // the ring entry it needs.  After the last unit of its range it stays.
+  Chunk<FMT> ring[P][kR];
+  // scale and bias in separate registers: combining them at load time would
+  // force a wait for every load in flight
+  uint16_t ssr[P][kR], bbr[P][kR];
+  int fTs = 1, ft = 0, fleft = 0;
+  uint32_t fwrow = 0, fsrow = 0, fc0 = 0, fc = 0;
+  auto fetch_start = [&](int s) {
+    fTs = seg_tiles(s);
+    const int Us = G * fTs;
+    const int a = range_lo_of(slot, Us);
+    const int g = a / fTs;
+    ft = a - g * fTs;
+    fleft = range_lo_of(slot + 1, Us) - a;
+    const uint32_t row = (uint32_t)(base + g * kR);
+    fwrow = row * (uint32_t)p.row_bytes;
+    fsrow = row * (uint32_t)p.G;
+    fc0 = (uint32_t)(s * ST * kKL + kl);
+    fc = fc0 + (uint32_t)(ft * kKL);
+  };
+  auto fetch = [&](Chunk<FMT>(&dst)[kR], uint16_t(&ss)[kR], uint16_t(&bs)[kR]) {
+    const uint32_t gi = (fc * 64u) / (uint32_t)GS;
+    const uint32_t wo = fwrow + fc * (uint32_t)F::CB;
+    const uint32_t so = 2u * (fsrow + gi);
 #pragma unroll
-  for (int r = 0; r < RCAP; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-
-  Chunk<FMT, GS> wc[RCAP];
-  half_t sc[RCAP], bc[RCAP];
-
-  auto fetch = [&](int tile, Chunk<FMT, GS>(&dst)[RCAP], half_t(&sdst)[RCAP], half_t(&bdst)[RCAP]) {
-    const int c = tile * TC + kl;
-    if (c < nchunks) {
-      const int g = (c * F::CH) / GS;
-#pragma unroll
-      for (int r = 0; r < RCAP; ++r) {
-        if (r < nrows) {
-          const int row = base + slot + r * SLOTS;
-          load_chunk<FMT, GS>(dst[r], p.w, row, c, p.row_bytes);
-          sdst[r] = p.s[(size_t)row * p.G + g];
-          if constexpr (!IMPLIED) bdst[r] = p.b[(size_t)row * p.G + g];
-        }
+    for (int r = 0; r < kR; ++r) {
+      load_chunk<FMT>(dst[r], rw, wo, r * p.row_bytes);
+      ss[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, r * 2 * p.G, 0);
+      if constexpr (!IMPLIED) bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, r * 2 * p.G, 0);
+      else bs[r] = 0;
+    }
+    if (fleft > 1) {
+      --fleft;
+      fc += kKL;
+      if (++ft == fTs) {
+        ft = 0;
+        fc = fc0;
+        fwrow += kR * (uint32_t)p.row_bytes;
+        fsrow += kR * (uint32_t)p.G;
       }
     }
   };
 
-  __syncthreads();
-  stage_tile<FMT, GS, M>(p, 0, xs, xsum);
-  fetch(0, wc, sc, bc);
-  __syncthreads();
+  // accumulators hold y * 2^-24: the scaled products' unit
+  float acc[kR][M];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+  int run_g = -1, run_uid = 0;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    Chunk<FMT, GS> wn[RCAP];
-    half_t sn[RCAP], bn[RCAP];
-    if (t + 1 < ntiles) {
-      stage_tile<FMT, GS, M>(p, t + 1, xs + (cur ^ 1) * XT, xsum + (cur ^ 1) * M * TC);
-      fetch(t + 1, wn, sn, bn);
-    }
-    const int c = t * TC + kl;
-    if (c < nchunks) {
-      float P[RCAP][M];
+  // a run's sum over the slot's lanes goes to part[first unit of the run]
+  auto flush = [&]() {
+    if (run_g >= 0) {
 #pragma unroll
-      for (int r = 0; r < RCAP; ++r)
+      for (int r = 0; r < kR; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) P[r][m] = 0.f;
-      const uint32_t* xc = xs + cur * XT + kl * F::XD;
-      chunk_dot<FMT, GS, M, RCAP>(wc, xc, TC * F::XD, lut, nrows, sh, P);
-      const float* xsm = xsum + cur * M * TC + kl;
-#pragma unroll
-      for (int r = 0; r < RCAP; ++r) {
-        if (r < nrows) {
-          const float s = h2f(sc[r]);
-          const float s24 = s * 16777216.0f;
-          float b;
-          if constexpr (IMPLIED) b = -s * p.ratio;
-          else b = h2f(bc[r]);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float a = __builtin_fmaf(b, xsm[m * TC], acc[r][m]);
-            acc[r][m] = __builtin_fmaf(s24, P[r][m], a);
-          }
+        for (int m = 0; m < M; ++m) {
+          const float v = row_sum16(acc[r][m]);
+          if (kl == kKL - 1) part[run_uid * (kR * M) + r * M + m] = v;
+          acc[r][m] = 0.f;
         }
-      }
     }
-    __syncthreads();
-    if (t + 1 < ntiles) {
+    run_g = -1;
+  };
+
+  int cg = 0, ct = 0;  // compute cursor (row-group, tile within the segment)
+  auto process = [&](int s, int Ts, const Chunk<FMT>(&wc)[kR], const uint16_t(&ss)[kR],
+                     const uint16_t(&bs)[kR]) {
+    if (cg != run_g) {
+      flush();
+      run_g = cg;
+      run_uid = G * s * ST + cg * Ts + ct;
+    }
+    const int cs = ct * kKL + kl;  // chunk within the staged segment
+    const bool valid = (s * ST + ct) * kKL + kl < nchunks;
+    float Pd[kR][M];
 #pragma unroll
-      for (int r = 0; r < RCAP; ++r) {
-        wc[r] = wn[r];
-        sc[r] = sn[r];
-        bc[r] = bn[r];
+    for (int r = 0; r < kR; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) Pd[r][m] = 0.f;
+    chunk_dot<FMT, M>(wc, xs + cs * CS, lut, sh, Pd);
+    float X[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) X[m] = xsum[cs * M + m];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      // a chunk past K contributes 0
+      const float sc = valid ? h2f(__builtin_bit_cast(half_t, ss[r])) : 0.f;
+      const float bb = IMPLIED ? -sc * p.ratio : (valid ? h2f(__builtin_bit_cast(half_t, bs[r])) : 0.f);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float a = __builtin_fmaf(sc, Pd[r][m], acc[r][m]);
+        acc[r][m] = __builtin_fmaf(bb, X[m], a);
       }
     }
+    if (++ct == Ts) {
+      ct = 0;
+      ++cg;
+    }
+  };
+
+  // ring fill for segment 0 (after the x loads); a slot without units
+  // loads rows past its workgroup's (clamped by the descriptors), unused
+  fetch_start(0);
+#pragma unroll
+  for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
+  lds_barrier();  // LDS cleared, table built
+#pragma unroll
+  for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(p, 0, seg_tiles(0), xst[k], xs, xsum);
+  lds_barrier();
+
+  for (int s = 0; s < p.nseg; ++s) {
+    const int Ts = seg_tiles(s);
+    const int a = range_lo_of(slot, G * Ts), b = range_lo_of(slot + 1, G * Ts);
+    cg = a / Ts;
+    ct = a - cg * Ts;
+    for (int i = a; i < b; i += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if (i + j < b) process(s, Ts, ring[j], ssr[j], bbr[j]);
+        fetch(ring[j], ssr[j], bbr[j]);
+      }
+    }
+    flush();
+    if (s + 1 < p.nseg) {
+#pragma unroll
+      for (int k = 0; k < kStageRounds; ++k)
+        xstage_issue<FMT, GS, M>(p, rx, (s + 1) * ST, seg_tiles(s + 1), tid + k * kThreads, xst[k]);
+      fetch_start(s + 1);
+#pragma unroll
+      for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
+      lds_barrier();  // every slot is done with segment s
+#pragma unroll
+      for (int k = 0; k < kStageRounds; ++k)
+        xstage_commit<FMT, GS, M>(p, (s + 1) * ST, seg_tiles(s + 1), xst[k], xs, xsum);
+    }
+    lds_barrier();
   }
 
-#pragma unroll
-  for (int r = 0; r < RCAP; ++r) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float v = lane_sum<F::KL>(acc[r][m]);
-      const int row = base + slot + r * SLOTS;
-      if (kl == 0 && r < nrows) p.y[(size_t)m * p.N + row] = (half_t)v;
+  // every row adds its runs in unit order: in segment s, row-group g's units
+  // [g*Ts, (g+1)*Ts) are covered by consecutive slots, each run keyed by its
+  // first unit
+  for (int idx = tid; idx < G * kR * M; idx += kThreads) {
+    const int g = idx / (kR * M);
+    const int r = (idx / M) % kR;
+    const int m = idx % M;
+    if (g * kR + r >= nrow_wg) continue;
+    float v = 0.f;
+    for (int s = 0; s < p.nseg; ++s) {
+      const int Ts = seg_tiles(s);
+      const int Us = G * Ts;
+      const int u0 = g * Ts, u1 = u0 + Ts - 1;
+      const int k0 = ((u0 + 1) * kSlots - 1) / Us;   // slot holding unit u0
+      const int k1 = ((u1 + 1) * kSlots - 1) / Us;   // slot holding unit u1
+      for (int k = k0; k <= k1; ++k) {
+        const int lo = range_lo_of(k, Us), hi = range_lo_of(k + 1, Us);
+        if (lo < hi) v += part[(G * s * ST + max(u0, lo)) * (kR * M) + r * M + m];
+      }
     }
+    p.y[(size_t)m * p.N + base + g * kR + r] = (half_t)(v * 16777216.0f);  // * 2^24
   }
 }
 

@@ -40,8 +40,11 @@
  * names it.  A failed launch returns BQ_ERR_HIP.  Nothing aborts or throws
  * across this interface.
  *
- * Alignment: x, scales, biases and y need 2-byte alignment; w needs 4-byte
- * alignment (uint32 words for bits 1/2; dword loads for t5).  The t5 entry
+ * Alignment: x needs 16-byte alignment (it is read in 16-byte vectors);
+ * scales, biases and y need 2-byte alignment, except that bq_dequant with
+ * bits 1/2 writes y in 16-byte vectors and needs it 16-byte aligned; w needs
+ * 4-byte alignment (uint32 words for bits 1/2; dword loads for t5).  Fresh
+ * allocations from hipMalloc or torch meet all of these.  The t5 entry
  * points additionally need K to be a multiple of 256, so that every packed
  * row is a whole number of dwords (true of all the decoder shapes).
  */
