@@ -35,7 +35,7 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
     return BQ_ERR_BITS;
   }
   if (gs != 64 && gs != 128) return BQ_ERR_GROUP;
-  if (N <= 0 || K <= 0 || K % gs != 0 || K > (1 << 30)) return BQ_ERR_SHAPE;
+  if (N <= 0 || K <= 0 || K % gs != 0 || K > (1 << 26)) return BQ_ERR_SHAPE;
   // packed rows and scale rows are addressed with 32-bit offsets
   if ((uint64_t)N * (uint64_t)row_bytes_of(bits == BQ_BITS_T5 ? BQ_BITS_T5 : 2, K, gs) >= (1ull << 30) ||
       (uint64_t)N * (uint64_t)(K / gs) >= (1ull << 29))

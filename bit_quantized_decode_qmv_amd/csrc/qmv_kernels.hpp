@@ -246,18 +246,19 @@ template <> struct Chunk<FMT_U2> { u32x4 v; };
 template <> struct Chunk<FMT_U1> { u32x2 v; };
 template <> struct Chunk<FMT_T5> { u32x4 v; };
 
-// `off` (per lane) + `soff` (uniform) bytes into the packed rows.
+// The chunk at byte `off` of the packed rows.  The whole offset goes in the
+// per-lane operand: only that operand is range-checked against the
+// descriptor, so an offset past the end reads zeros and touches no memory.
 template <int FMT>
-__device__ __forceinline__ void load_chunk(Chunk<FMT>& c, rsrc_t w, uint32_t off, int soff) {
+__device__ __forceinline__ void load_chunk(Chunk<FMT>& c, rsrc_t w, uint32_t off) {
   if constexpr (FMT == FMT_U2) {
-    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)off, soff, 0);
+    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)off, 0, 0);
   } else if constexpr (FMT == FMT_U1) {
-    c.v = __builtin_amdgcn_raw_buffer_load_b64(w, (int)off, soff, 0);
+    c.v = __builtin_amdgcn_raw_buffer_load_b64(w, (int)off, 0, 0);
   } else {
-    // 13 bytes at off + soff; rows are whole dwords (soff a multiple of 4),
-    // so the dword-aligned 16-byte window that holds them never passes the
-    // end of the row.
-    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)(off & ~3u), soff, 0);
+    // 13 bytes at off; rows are whole dwords, so the dword-aligned 16-byte
+    // window that holds them never passes the end of the row.
+    c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)(off & ~3u), 0, 0);
   }
 }
 
@@ -266,42 +267,60 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT>& c, rsrc_t w, uint32_t off
 // chunk): one thread loads the chunk's 64 x values (65/63 for the halves of
 // a t5 128-group), writes its staged dwords (permuted into the order the
 // unpack produces code pairs, pre-scaled by 2^-e) with 16-byte LDS stores
-// and its sum of x.  xstage_issue loads into registers, xstage_commit
-// writes LDS, so that other loads can be issued in between.
+// and its sum of x.  xstage_plan does the index arithmetic (before any load
+// is in flight), xstage_load loads into registers and xstage_commit writes
+// LDS, so that other loads can be issued in between.
 // --------------------------------------------------------------------------
 template <int FMT, int GS> struct XSpan {
-  // x dwords a task loads (as 16-byte vectors) and the code offset of the
-  // first one relative to the chunk's nominal start 64*c
-  static constexpr int VEC = (FMT == FMT_T5 && GS == 128) ? 9 : 8;
+  // the halves of a t5 128-group need one x dword past the chunk's 64 codes
+  static constexpr bool TAIL = FMT == FMT_T5 && GS == 128;
 };
 
-template <int FMT, int GS> struct XStage { u32x4 v[XSpan<FMT, GS>::VEC]; int task; };
+// 64 x values from the chunk's nominal start (8 16-byte vectors) and, for
+// t5 128-groups, the dword after them; where they go
+template <int FMT, int GS> struct XStage {
+  u32x4 v[8];
+  uint32_t tail;
+  uint32_t off;  // byte offset in x
+  int c;         // chunk within its tile
+  int dst;       // staged dwords: xs + dst
+  int xi;        // sum of x: xsum[xi]
+  bool live;     // the thread has a task
+  bool wave;     // some thread of the wave has a task
+};
 constexpr int kStageRounds = 2;  // staging tasks per thread
 
 template <int FMT, int GS, int M>
-__device__ __forceinline__ void xstage_issue(const QmvParams& p, rsrc_t rx, int s0, int Ts, int task,
-                                             XStage<FMT, GS>& st) {
-  constexpr int VEC = XSpan<FMT, GS>::VEC;
-  st.task = task;
+__device__ __forceinline__ void xstage_plan(const QmvParams& p, int s0, int Ts, int task, XStage<FMT, GS>& st) {
+  const int ntask = M * Ts * kKL;
   const int c = task % kKL, tt = (task / kKL) % Ts, m = min(task / (kKL * Ts), M);
+  st.c = c;
+  st.dst = (tt * kKL + c) * chunk_stride<M>() + m * kXD;
+  st.xi = (tt * kKL + c) * M + m;
+  st.live = task < ntask;
+  st.wave = ((int)threadIdx.x & ~63) + (task - (int)threadIdx.x) < ntask;
   // the chunk's nominal first code; t5 128-groups: chunk 2g loads from code
-  // 128g, chunk 2g+1 from 128g+64 (both 16-byte aligned).  Loads are always
-  // issued; a task past M reads past the end of x (zeros), unused anyway.
-  const uint32_t off = 2u * ((uint32_t)m * (uint32_t)p.K + (uint32_t)((s0 + tt) * kTile + 64 * c));
+  // 128g, chunk 2g+1 from 128g+64 (both 16-byte aligned).  A chunk past K
+  // loads from an offset with bit 31 set (x is below 2^30 bytes): out of the
+  // descriptor's range, it reads zeros, so the chunk stages zeros.
+  const int k0 = (s0 + tt) * kTile + 64 * c;
+  st.off = (2u * ((uint32_t)m * (uint32_t)p.K + (uint32_t)k0)) | (k0 < p.K ? 0u : 0x80000000u);
+}
+
+template <int FMT, int GS>
+__device__ __forceinline__ void xstage_load(rsrc_t rx, XStage<FMT, GS>& st) {
+  if (!st.wave) return;  // whole waves without a task issue nothing
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16u * j), 0, 0);
+  for (int j = 0; j < 8; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(st.off + 16u * j), 0, 0);
+  if constexpr (XSpan<FMT, GS>::TAIL) st.tail = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(st.off + 128u), 0, 0);
 }
 
 template <int FMT, int GS, int M>
-__device__ __forceinline__ void xstage_commit(const QmvParams& p, int s0, int Ts, const XStage<FMT, GS>& st,
-                                              uint32_t* xs, float* xsum) {
-  const int task = st.task;
-  if (task >= M * Ts * kKL) return;  // whole waves without a task skip the work
-  const int c = task % kKL, tt = (task / kKL) % Ts, m = task / (kKL * Ts);
-  const int k0 = (s0 + tt) * kTile + 64 * c;
-  const bool live = k0 < p.K;
+__device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_t* xs, float* xsum) {
+  if (!st.live) return;
+  const int c = st.c;
   // X[j] = (x[2j], x[2j+1]) of the loaded span
-  auto X = [&](int j) -> uint32_t { return st.v[j >> 2][j & 3]; };
+  auto X = [&](int j) -> uint32_t { return j < 32 ? st.v[j >> 2][j & 3] : st.tail; };
   auto H = [&](int k) -> uint32_t { return (X(k >> 1) >> (16 * (k & 1))) & 0xFFFFu; };  // x[k] bits
   auto P2 = [&](int k0_, int k1_, int e) -> uint32_t {  // (x[k0], x[k1]) * 2^-e; k < 0 means 0
     const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
@@ -381,13 +400,13 @@ __device__ __forceinline__ void xstage_commit(const QmvParams& p, int s0, int Ts
     const float other = __shfl_xor(sum, 1, 64);
     sum = (c & 1) ? 0.f : sum + other;
   }
-  if (live) {
-    uint32_t* dst = xs + (tt * kKL + c) * chunk_stride<M>() + m * kXD;
+  // every staged chunk of the segment is written (chunks past K with zeros),
+  // so LDS needs no clearing
+  uint32_t* dst = xs + st.dst;
 #pragma unroll
-    for (int q = 0; q < 9; ++q)
-      *reinterpret_cast<u32x4*>(dst + 4 * q) = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-    xsum[(tt * kKL + c) * M + m] = sum * 5.9604644775390625e-08f;  // * 2^-24, like the products
-  }
+  for (int q = 0; q < 9; ++q)
+    *reinterpret_cast<u32x4*>(dst + 4 * q) = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+  xsum[st.xi] = sum * 5.9604644775390625e-08f;  // * 2^-24, like the products
 }
 
 // --------------------------------------------------------------------------
@@ -532,21 +551,20 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   // x of segment 0 first, so that waiting for it never waits for W
   XStage<FMT, GS> xst[kStageRounds];
 #pragma unroll
-  for (int k = 0; k < kStageRounds; ++k) xstage_issue<FMT, GS, M>(p, rx, 0, min(ST, T), tid + k * kThreads, xst[k]);
+  for (int k = 0; k < kStageRounds; ++k) xstage_plan<FMT, GS, M>(p, 0, min(ST, T), tid + k * kThreads, xst[k]);
+#pragma unroll
+  for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
 
-  for (int i = tid; i < ST * kKL * CS; i += kThreads) xs[i] = 0u;
-  if constexpr (FMT == FMT_T5) {
-    if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
-  }
 
   auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
   // slot k's units of segment s: [lo(k), lo(k+1)) with lo(k) = k*U_s/kSlots
   auto range_lo_of = [&](int k, int Us) { return (k * Us) / kSlots; };
 
   // ---- fetch cursor: unit (row-group, tile ft) of the current segment.
-  // Every unit issues the same loads (rows past N and chunks past K read
+  // Every fetch issues the same loads (rows past N and chunks past K read
   // zeros or data that is never used), so the compiler can wait for exactly
-  // the ring entry it needs.  After the last unit of its range it stays.
+  // the ring entry it needs.  Fetches past the slot's range use an offset
+  // outside every buffer: no memory is touched and zeros come back.
   Chunk<FMT> ring[P][kR];
   // scale and bias in separate registers: combining them at load time would
   // force a wait for every load in flight
@@ -568,16 +586,22 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   };
   auto fetch = [&](Chunk<FMT>(&dst)[kR], uint16_t(&ss)[kR], uint16_t(&bs)[kR]) {
     const uint32_t gi = (fc * 64u) / (uint32_t)GS;
-    const uint32_t wo = fwrow + fc * (uint32_t)F::CB;
+    const bool live = fleft > 0;
+    // buffers are below 2^30 bytes: bit 31 puts a dead fetch out of range
+    const uint32_t dead = live ? 0u : 0x80000000u;
+    // 24-bit multiply (fc < 2^20): a 64-bit multiply-add here would read a
+    // don't-care register that may still be the target of a load in flight
+    const uint32_t wo = fwrow + __umul24(fc, (uint32_t)F::CB);
     const uint32_t so = 2u * (fsrow + gi);
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-      load_chunk<FMT>(dst[r], rw, wo, r * p.row_bytes);
-      ss[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, r * 2 * p.G, 0);
-      if constexpr (!IMPLIED) bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, r * 2 * p.G, 0);
+      load_chunk<FMT>(dst[r], rw, (wo + (uint32_t)(r * p.row_bytes)) | dead);
+      const int sor = (int)((so + (uint32_t)(r * 2 * p.G)) | dead);
+      ss[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, sor, 0, 0);
+      if constexpr (!IMPLIED) bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, sor, 0, 0);
       else bs[r] = 0;
     }
-    if (fleft > 1) {
+    if (live) {
       --fleft;
       fc += kKL;
       if (++ft == fTs) {
@@ -649,14 +673,16 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   };
 
   // ring fill for segment 0 (after the x loads); a slot without units
-  // loads rows past its workgroup's (clamped by the descriptors), unused
+  // fetches nothing
   fetch_start(0);
 #pragma unroll
   for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
-  lds_barrier();  // LDS cleared, table built
+  if constexpr (FMT == FMT_T5) {
+    if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
+  }
 #pragma unroll
-  for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(p, 0, seg_tiles(0), xst[k], xs, xsum);
-  lds_barrier();
+  for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
+  lds_barrier();  // x of segment 0 staged, table built
 
   for (int s = 0; s < p.nseg; ++s) {
     const int Ts = seg_tiles(s);
@@ -674,14 +700,16 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
     if (s + 1 < p.nseg) {
 #pragma unroll
       for (int k = 0; k < kStageRounds; ++k)
-        xstage_issue<FMT, GS, M>(p, rx, (s + 1) * ST, seg_tiles(s + 1), tid + k * kThreads, xst[k]);
+        xstage_plan<FMT, GS, M>(p, (s + 1) * ST, seg_tiles(s + 1), tid + k * kThreads, xst[k]);
+#pragma unroll
+      for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
       fetch_start(s + 1);
 #pragma unroll
       for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
       lds_barrier();  // every slot is done with segment s
 #pragma unroll
       for (int k = 0; k < kStageRounds; ++k)
-        xstage_commit<FMT, GS, M>(p, (s + 1) * ST, seg_tiles(s + 1), xst[k], xs, xsum);
+        xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
     }
     lds_barrier();
   }

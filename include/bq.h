@@ -64,7 +64,9 @@ typedef enum bq_status {
   BQ_ERR_NULL = -1,       /* a required pointer is NULL */
   BQ_ERR_BITS = -2,       /* bits not valid for this entry point */
   BQ_ERR_GROUP = -3,      /* group_size not 64 or 128 */
-  BQ_ERR_SHAPE = -4,      /* N or K not positive, K % group_size != 0, or size overflow */
+  BQ_ERR_SHAPE = -4,      /* N or K not positive, K % group_size != 0, K > 2^26,
+                             or N * (packed row bytes) >= 2^30, or
+                             N * (K / group_size) >= 2^29 (32-bit offsets) */
   BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
   BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
   BQ_ERR_HIP = -7         /* the HIP runtime rejected a launch */

@@ -116,6 +116,8 @@ def test_shapes(lib, name):
     assert call(lib, name, bits=bits, K=0) == SHAPE
     assert call(lib, name, bits=bits, K=320, gs=128) == SHAPE
     assert call(lib, name, bits=bits, K=(1 << 30) + 1024) == SHAPE
+    assert call(lib, name, bits=bits, N=1, K=(1 << 26) + 1024) == SHAPE
+    assert call(lib, name, bits=bits, N=8192, K=1 << 20) == SHAPE  # packed rows past 2^30 bytes
 
 
 @pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES)
