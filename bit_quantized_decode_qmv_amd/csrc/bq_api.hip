@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bq.h"
 #include "dequant_kernels.hpp"
 #include "qmm_kernels.hpp"
@@ -49,6 +51,10 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if (!aligned(y, 2)) return BQ_ERR_ALIGN;
   if (bits == BQ_BITS_T5 && K % 256 != 0) return BQ_ERR_ALIGN;
   if (e != E_DEQUANT && !aligned(x, 16)) return BQ_ERR_ALIGN;
+  // the decode kernels read scales and biases in 16-byte vectors
+  if (e != E_DEQUANT && e != E_QMM &&
+      (!aligned(scales, 16) || (biases && e != E_SYM && !aligned(biases, 16))))
+    return BQ_ERR_ALIGN;
   if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
   return BQ_OK;
 }
@@ -60,44 +66,74 @@ int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, vo
 }
 
 // ---------------------------------------------------------------- qmv family
-// Units kept in flight per slot (free to depend on M: it never changes the
-// arithmetic).
-template <int M> constexpr int ring_depth() { return 4; }
-constexpr int kSegTiles = 9;  // K tiles per x segment in LDS
-static_assert(kSegTiles * kKL * BQ_MAX_WIDE_M <= kStageRounds * kThreads, "x staging tasks per thread");
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxRowsPerWg = 256;
 constexpr size_t kLdsBudget = 150 * 1024;
 
-size_t qmv_lds_bytes(int M, int rows_per_wg, int ntiles, int seg_tiles) {
+// 16-byte vectors of a workgroup's scale (or bias) block, at most
+int sb_vectors(int rows_per_wg, int G) { return (int)(((int64_t)rows_per_wg * G * 2 + 15) / 16 + 1); }
+
+size_t qmv_lds_bytes(int M, int rows_per_wg, int ntiles, int seg_tiles, int G) {
   const size_t U = (size_t)((rows_per_wg + kR - 1) / kR) * ntiles;
   const size_t cs = (size_t)M * kXD + ((M % 2 == 0) ? 4 : 0);
-  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL + U * kR * M);
+  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL + 8 * (size_t)sb_vectors(rows_per_wg, G) +
+              U * kR * M);
 }
 
-// Workgroup geometry: a function of N and K only, never of M.
-void qmv_geometry(QmvParams& p) {
+// Workgroup geometry for M activation rows.  Rows per workgroup: enough for
+// one workgroup per CU.  Segment: as many K tiles of x as LDS and the
+// staging tasks (M * tiles * 16 <= kStageRounds * kThreads) allow, split
+// evenly.  Returns false if even two rows per workgroup do not fit.
+bool qmv_geometry(QmvParams& p, int M) {
   p.ntiles = (p.K + kTile - 1) / kTile;
-  p.seg_tiles = p.ntiles < kSegTiles ? p.ntiles : kSegTiles;
-  p.nseg = (p.ntiles + p.seg_tiles - 1) / p.seg_tiles;
+  const int max_st = std::min(p.ntiles, kStageRounds * kThreads / (kKL * M));
   int rows = kR * ((p.N + kR * kTargetWorkgroups - 1) / (kR * kTargetWorkgroups));
   if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
-  while (rows > kR && qmv_lds_bytes(BQ_MAX_WIDE_M, rows, p.ntiles, p.seg_tiles) > kLdsBudget) rows -= kR;
-  p.rows_per_wg = rows;
+  for (; rows >= kR; rows -= kR) {
+    if (sb_vectors(rows, p.G) > kSbRounds * kThreads) continue;
+    int st = max_st;
+    while (st > 0 && qmv_lds_bytes(M, rows, p.ntiles, st, p.G) > kLdsBudget) --st;
+    if (st == 0) continue;
+    p.nseg = (p.ntiles + st - 1) / st;
+    p.seg_tiles = (p.ntiles + p.nseg - 1) / p.nseg;
+    p.rows_per_wg = rows;
+    p.sb_dwords = 8 * sb_vectors(rows, p.G);
+    return true;
+  }
+  return false;
 }
 
-template <int FMT, int GS, int M, bool IMPLIED>
-int launch_qmv_t(QmvParams p, void* stream) {
-  constexpr int P = ring_depth<M>();
-  qmv_geometry(p);
-  const size_t shmem = qmv_lds_bytes(M, p.rows_per_wg, p.ntiles, p.seg_tiles);
-  if (shmem > kLdsBudget) return BQ_ERR_SHAPE;
+// Units each slot keeps in flight: enough to cover a slot's share of a
+// segment where that is small, so that few loads are issued for nothing.
+// The ring depth never changes the arithmetic.
+int units_per_slot(const QmvParams& p) {
+  const int U = ((p.rows_per_wg + kR - 1) / kR) * p.seg_tiles;
+  return (U + kSlots - 1) / kSlots;
+}
+
+template <int FMT, int GS, int M, bool IMPLIED, int P>
+int launch_qmv_p(const QmvParams& p, void* stream) {
   const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
   (void)attr;
+  const size_t shmem = qmv_lds_bytes(M, p.rows_per_wg, p.ntiles, p.seg_tiles, p.G);
   dim3 grid((p.N + p.rows_per_wg - 1) / p.rows_per_wg);
-  return launch(fn, grid, dim3(kThreads), shmem, stream, &p);
+  QmvParams q = p;
+  return launch(fn, grid, dim3(kThreads), shmem, stream, &q);
+}
+
+template <int FMT, int GS, int M, bool IMPLIED>
+int launch_qmv_t(QmvParams p, void* stream) {
+  if (!qmv_geometry(p, M)) return BQ_ERR_SHAPE;
+  if constexpr (M == 1) {
+    const int ups = units_per_slot(p);
+    if (ups <= 2) return launch_qmv_p<FMT, GS, M, IMPLIED, 2>(p, stream);
+    if (ups <= 4) return launch_qmv_p<FMT, GS, M, IMPLIED, 4>(p, stream);
+    return launch_qmv_p<FMT, GS, M, IMPLIED, 6>(p, stream);
+  } else {
+    return launch_qmv_p<FMT, GS, M, IMPLIED, 4>(p, stream);
+  }
 }
 
 typedef int (*QmvLauncher)(QmvParams, void*);
@@ -175,7 +211,9 @@ const char* bq_strerror(int status) {
     case BQ_ERR_GROUP: return "group_size must be 64 or 128";
     case BQ_ERR_SHAPE: return "N and K must be positive, K a multiple of group_size and at most 2^30";
     case BQ_ERR_M: return "M is outside the range this entry point accepts";
-    case BQ_ERR_ALIGN: return "a pointer is misaligned (x needs 16 bytes), or a t5 call has K not a multiple of 256";
+    case BQ_ERR_ALIGN:
+      return "a pointer is misaligned (x, and for the decode calls scales and biases, need 16 bytes), or a t5 "
+             "call has K not a multiple of 256";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown bq status";

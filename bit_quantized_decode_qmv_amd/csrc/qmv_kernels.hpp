@@ -77,6 +77,7 @@ struct QmvParams {
   int x_bytes;           // M * K * 2 (buffer descriptor size)
   int w_bytes;           // N * row_bytes (buffer descriptor size)
   int sb_bytes;          // N * G * 2
+  int sb_dwords;         // LDS dwords of the staged scale/bias block
   float ratio;           // implied bias = -scale * ratio
 };
 
@@ -410,6 +411,52 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
 }
 
 // --------------------------------------------------------------------------
+// Scale/bias staging.  A workgroup's rows are contiguous in the [N][G] scale
+// and bias arrays, so its block is one byte range; it is read with 16-byte
+// loads from the aligned address at or below its start and stored in LDS as
+// (scale, bias) half pairs, one dword per (row, group), dword 8v+i holding
+// element i of vector v.  Element (row, group) of the block then sits at
+// dword delta + row*G + group, delta = (start mod 16) / 2.
+// --------------------------------------------------------------------------
+constexpr int kSbRounds = 2;  // 16-byte vectors per thread and array
+
+struct SbStage {
+  u32x4 s[kSbRounds], b[kSbRounds];
+  int nvec;
+};
+
+template <bool IMPLIED>
+__device__ __forceinline__ void sbstage_load(rsrc_t rs, rsrc_t rb, uint32_t lo_al, int nvec, SbStage& st) {
+  st.nvec = nvec;
+#pragma unroll
+  for (int k = 0; k < kSbRounds; ++k) {
+    const int v = (int)threadIdx.x + k * kThreads;
+    const int off = (int)((lo_al + 16u * (uint32_t)v) | (v < nvec ? 0u : 0x80000000u));
+    st.s[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    if constexpr (!IMPLIED) st.b[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+  }
+}
+
+template <bool IMPLIED>
+__device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl) {
+#pragma unroll
+  for (int k = 0; k < kSbRounds; ++k) {
+    const int v = (int)threadIdx.x + k * kThreads;
+    if (v < st.nvec) {
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sv = st.s[k][j], bv = IMPLIED ? 0u : st.b[k][j];
+        o[2 * j] = __builtin_amdgcn_perm(bv, sv, 0x05040100u);      // (s lo, b lo)
+        o[2 * j + 1] = __builtin_amdgcn_perm(bv, sv, 0x07060302u);  // (s hi, b hi)
+      }
+      *reinterpret_cast<u32x4*>(sbl + 8 * v) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4*>(sbl + 8 * v + 4) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // Per-chunk multiply: Pd[r][m] = codes(row r) . xstaged(m).
 // xc points at the lane's staged chunk; row m of x is kXD dwords further.
 // --------------------------------------------------------------------------
@@ -531,22 +578,26 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
 
   const int ST = p.seg_tiles;
   const int T = p.ntiles;
-  uint32_t* xs = smem;                                             // [ST*16][CS]
-  float* xsum = reinterpret_cast<float*>(smem + ST * kKL * CS);    // [ST*16][M]
-  float* part = xsum + ST * kKL * M;                               // [U][kR*M]
+  uint32_t* xs = smem;                                              // [ST*16][CS]
+  float* xsum = reinterpret_cast<float*>(smem + ST * kKL * CS);     // [ST*16][M]
+  uint32_t* sbl = reinterpret_cast<uint32_t*>(xsum + ST * kKL * M);  // [sb_dwords]
+  float* part = reinterpret_cast<float*>(sbl + p.sb_dwords);        // [NG*T][kR*M]
 
   const int tid = threadIdx.x;
   const int slot = tid / kKL;
   const int kl = tid % kKL;
   const int base = blockIdx.x * p.rows_per_wg;
   const int nrow_wg = min(p.rows_per_wg, p.N - base);
-  const int G = (nrow_wg + kR - 1) / kR;
+  const int NG = (nrow_wg + kR - 1) / kR;  // row-groups of this workgroup
   const int nchunks = p.K / 64;
   const uint32_t sh = (uint32_t)(kl & 3);  // t5 run offset inside its first dword
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
-  const rsrc_t rs = make_rsrc(p.s, p.sb_bytes);
-  const rsrc_t rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  // the workgroup's scale/bias block: bytes [sb_lo, sb_lo + nrow_wg*G*2)
+  const uint32_t sb_lo = (uint32_t)base * (uint32_t)p.G * 2u;
+  const uint32_t sb_lo_al = sb_lo & ~15u;
+  const int sb_delta = (int)(sb_lo - sb_lo_al) / 2;
+  const int sb_nvec = (int)((sb_lo + (uint32_t)nrow_wg * (uint32_t)p.G * 2u - sb_lo_al + 15u) >> 4);
 
   // x of segment 0 first, so that waiting for it never waits for W
   XStage<FMT, GS> xst[kStageRounds];
@@ -554,7 +605,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   for (int k = 0; k < kStageRounds; ++k) xstage_plan<FMT, GS, M>(p, 0, min(ST, T), tid + k * kThreads, xst[k]);
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
-
+  // The range check zeroes whole dwords that reach past the descriptor's
+  // size, so the size is rounded up to the 16-byte block that holds the last
+  // element; with a 16-byte aligned base that block never leaves the page.
+  SbStage sbst;
+  const int sb_size = (p.sb_bytes + 15) & ~15;
+  sbstage_load<IMPLIED>(make_rsrc(p.s, sb_size), make_rsrc(IMPLIED ? p.s : p.b, sb_size), sb_lo_al, sb_nvec, sbst);
 
   auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
   // slot k's units of segment s: [lo(k), lo(k+1)) with lo(k) = k*U_s/kSlots
@@ -566,41 +622,28 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   // the ring entry it needs.  Fetches past the slot's range use an offset
   // outside every buffer: no memory is touched and zeros come back.
   Chunk<FMT> ring[P][kR];
-  // scale and bias in separate registers: combining them at load time would
-  // force a wait for every load in flight
-  uint16_t ssr[P][kR], bbr[P][kR];
   int fTs = 1, ft = 0, fleft = 0;
-  uint32_t fwrow = 0, fsrow = 0, fc0 = 0, fc = 0;
+  uint32_t fwrow = 0, fc0 = 0, fc = 0;
   auto fetch_start = [&](int s) {
     fTs = seg_tiles(s);
-    const int Us = G * fTs;
+    const int Us = NG * fTs;
     const int a = range_lo_of(slot, Us);
     const int g = a / fTs;
     ft = a - g * fTs;
     fleft = range_lo_of(slot + 1, Us) - a;
-    const uint32_t row = (uint32_t)(base + g * kR);
-    fwrow = row * (uint32_t)p.row_bytes;
-    fsrow = row * (uint32_t)p.G;
+    fwrow = (uint32_t)(base + g * kR) * (uint32_t)p.row_bytes;
     fc0 = (uint32_t)(s * ST * kKL + kl);
     fc = fc0 + (uint32_t)(ft * kKL);
   };
-  auto fetch = [&](Chunk<FMT>(&dst)[kR], uint16_t(&ss)[kR], uint16_t(&bs)[kR]) {
-    const uint32_t gi = (fc * 64u) / (uint32_t)GS;
+  auto fetch = [&](Chunk<FMT>(&dst)[kR]) {
     const bool live = fleft > 0;
     // buffers are below 2^30 bytes: bit 31 puts a dead fetch out of range
     const uint32_t dead = live ? 0u : 0x80000000u;
     // 24-bit multiply (fc < 2^20): a 64-bit multiply-add here would read a
     // don't-care register that may still be the target of a load in flight
     const uint32_t wo = fwrow + __umul24(fc, (uint32_t)F::CB);
-    const uint32_t so = 2u * (fsrow + gi);
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      load_chunk<FMT>(dst[r], rw, (wo + (uint32_t)(r * p.row_bytes)) | dead);
-      const int sor = (int)((so + (uint32_t)(r * 2 * p.G)) | dead);
-      ss[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, sor, 0, 0);
-      if constexpr (!IMPLIED) bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rb, sor, 0, 0);
-      else bs[r] = 0;
-    }
+    for (int r = 0; r < kR; ++r) load_chunk<FMT>(dst[r], rw, (wo + (uint32_t)(r * p.row_bytes)) | dead);
     if (live) {
       --fleft;
       fc += kKL;
@@ -608,44 +651,26 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
         ft = 0;
         fc = fc0;
         fwrow += kR * (uint32_t)p.row_bytes;
-        fsrow += kR * (uint32_t)p.G;
       }
     }
   };
 
-  // accumulators hold y * 2^-24: the scaled products' unit
-  float acc[kR][M];
-#pragma unroll
-  for (int r = 0; r < kR; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-  int run_g = -1, run_uid = 0;
-
-  // a run's sum over the slot's lanes goes to part[first unit of the run]
-  auto flush = [&]() {
-    if (run_g >= 0) {
-#pragma unroll
-      for (int r = 0; r < kR; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float v = row_sum16(acc[r][m]);
-          if (kl == kKL - 1) part[run_uid * (kR * M) + r * M + m] = v;
-          acc[r][m] = 0.f;
-        }
-    }
-    run_g = -1;
-  };
-
+  // Each unit's partial products, summed over the slot's 16 lanes, go to
+  // part[(row-group * T + tile) * kR*M + r*M + m]; rows then add their tiles
+  // in order.  No sum depends on M, on the segment length or on which slot
+  // took the unit, so a row's result is the same in every such launch.
   int cg = 0, ct = 0;  // compute cursor (row-group, tile within the segment)
-  auto process = [&](int s, int Ts, const Chunk<FMT>(&wc)[kR], const uint16_t(&ss)[kR],
-                     const uint16_t(&bs)[kR]) {
-    if (cg != run_g) {
-      flush();
-      run_g = cg;
-      run_uid = G * s * ST + cg * Ts + ct;
-    }
+  auto process = [&](int s, int Ts, const Chunk<FMT>(&wc)[kR]) {
     const int cs = ct * kKL + kl;  // chunk within the staged segment
-    const bool valid = (s * ST + ct) * kKL + kl < nchunks;
+    const int tile = s * ST + ct;
+    const int chunk = tile * kKL + kl;
+    const bool valid = chunk < nchunks;
+    // (scale, bias) of both rows; chunks past K read the row's last group,
+    // unused
+    const int grp = min((chunk * 64) / GS, p.G - 1);
+    uint32_t sbv[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) sbv[r] = sbl[sb_delta + (cg * kR + r) * p.G + grp];
     float Pd[kR][M];
 #pragma unroll
     for (int r = 0; r < kR; ++r)
@@ -655,15 +680,16 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
     float X[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) X[m] = xsum[cs * M + m];
+    float* dst = part + (cg * T + tile) * (kR * M);
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       // a chunk past K contributes 0
-      const float sc = valid ? h2f(__builtin_bit_cast(half_t, ss[r])) : 0.f;
-      const float bb = IMPLIED ? -sc * p.ratio : (valid ? h2f(__builtin_bit_cast(half_t, bs[r])) : 0.f);
+      const float sc = valid ? lo_half(sbv[r]) : 0.f;
+      const float bb = IMPLIED ? -sc * p.ratio : (valid ? hi_half(sbv[r]) : 0.f);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float a = __builtin_fmaf(sc, Pd[r][m], acc[r][m]);
-        acc[r][m] = __builtin_fmaf(bb, X[m], a);
+        const float v = row_sum16(__builtin_fmaf(bb, X[m], sc * Pd[r][m]));
+        if (kl == kKL - 1) dst[r * M + m] = v;
       }
     }
     if (++ct == Ts) {
@@ -676,27 +702,27 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   // fetches nothing
   fetch_start(0);
 #pragma unroll
-  for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
+  for (int j = 0; j < P; ++j) fetch(ring[j]);
   if constexpr (FMT == FMT_T5) {
     if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
   }
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
-  lds_barrier();  // x of segment 0 staged, table built
+  sbstage_commit<IMPLIED>(sbst, sbl);
+  lds_barrier();  // x of segment 0, scales and biases staged; table built
 
   for (int s = 0; s < p.nseg; ++s) {
     const int Ts = seg_tiles(s);
-    const int a = range_lo_of(slot, G * Ts), b = range_lo_of(slot + 1, G * Ts);
+    const int a = range_lo_of(slot, NG * Ts), b = range_lo_of(slot + 1, NG * Ts);
     cg = a / Ts;
     ct = a - cg * Ts;
     for (int i = a; i < b; i += P) {
 #pragma unroll
       for (int j = 0; j < P; ++j) {
-        if (i + j < b) process(s, Ts, ring[j], ssr[j], bbr[j]);
-        fetch(ring[j], ssr[j], bbr[j]);
+        if (i + j < b) process(s, Ts, ring[j]);
+        fetch(ring[j]);
       }
     }
-    flush();
     if (s + 1 < p.nseg) {
 #pragma unroll
       for (int k = 0; k < kStageRounds; ++k)
@@ -705,36 +731,24 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
       for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
       fetch_start(s + 1);
 #pragma unroll
-      for (int j = 0; j < P; ++j) fetch(ring[j], ssr[j], bbr[j]);
+      for (int j = 0; j < P; ++j) fetch(ring[j]);
       lds_barrier();  // every slot is done with segment s
 #pragma unroll
-      for (int k = 0; k < kStageRounds; ++k)
-        xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
+      for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
     }
     lds_barrier();
   }
 
-  // every row adds its runs in unit order: in segment s, row-group g's units
-  // [g*Ts, (g+1)*Ts) are covered by consecutive slots, each run keyed by its
-  // first unit
-  for (int idx = tid; idx < G * kR * M; idx += kThreads) {
+  // y = sum over the row's tiles, in tile order, * 2^24
+  for (int idx = tid; idx < NG * kR * M; idx += kThreads) {
     const int g = idx / (kR * M);
-    const int r = (idx / M) % kR;
-    const int m = idx % M;
+    const int rm = idx - g * (kR * M);
+    const int r = rm / M, m = rm - r * M;
     if (g * kR + r >= nrow_wg) continue;
+    const float* src = part + g * T * (kR * M) + rm;
     float v = 0.f;
-    for (int s = 0; s < p.nseg; ++s) {
-      const int Ts = seg_tiles(s);
-      const int Us = G * Ts;
-      const int u0 = g * Ts, u1 = u0 + Ts - 1;
-      const int k0 = ((u0 + 1) * kSlots - 1) / Us;   // slot holding unit u0
-      const int k1 = ((u1 + 1) * kSlots - 1) / Us;   // slot holding unit u1
-      for (int k = k0; k <= k1; ++k) {
-        const int lo = range_lo_of(k, Us), hi = range_lo_of(k + 1, Us);
-        if (lo < hi) v += part[(G * s * ST + max(u0, lo)) * (kR * M) + r * M + m];
-      }
-    }
-    p.y[(size_t)m * p.N + base + g * kR + r] = (half_t)(v * 16777216.0f);  // * 2^24
+    for (int t = 0; t < T; ++t) v += src[t * (kR * M)];
+    p.y[(size_t)m * p.N + base + g * kR + r] = (half_t)(v * 16777216.0f);
   }
 }
 

@@ -151,6 +151,15 @@ def test_qmm_and_dequant_vector_alignment(lib):
     assert call(lib, "bq_dequant", bits=2, y=PY + 8) == ALIGN
 
 
+@pytest.mark.parametrize("name", ["bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide"])
+def test_decode_scale_bias_vector_alignment(lib, name):
+    # the decode kernels stage a workgroup's scales and biases with 16-byte loads
+    bits = 0 if name in T5_ENTRIES else 2
+    assert call(lib, name, bits=bits, s=PS + 8) == ALIGN
+    if name != "bq_qmv_sym":  # sym never reads the bias pointer
+        assert call(lib, name, bits=bits, b=PB + 8) == ALIGN
+
+
 def test_binding_raises_with_status(lib):
     with pytest.raises(bq.BQError) as ei:
         bq.bq_qmv_wide(PX, PW, PS, PB, PY, 6, 8, 256, 2, 64)
