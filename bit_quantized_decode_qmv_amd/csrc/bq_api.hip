@@ -14,6 +14,15 @@ namespace {
 
 using namespace bq;
 
+// 16-byte vectors of a workgroup's scale (or bias) block, at most
+constexpr int sb_vectors(int rows_per_wg, int G) { return (int)(((int64_t)rows_per_wg * G * 2 + 15) / 16 + 1); }
+// Groups per row the decode kernels take: the scale rows of two rows must
+// fit one staging pass.
+constexpr int kMaxDecodeGroups = 4092;
+static_assert(sb_vectors(bq::kR, kMaxDecodeGroups) <= bq::kSbRounds * bq::kThreads &&
+                  sb_vectors(bq::kR, kMaxDecodeGroups + 1) > bq::kSbRounds * bq::kThreads,
+              "decode group limit");
+
 enum Entry { E_QMV, E_WIDE, E_SYM, E_T5, E_T5_WIDE, E_QMM, E_DEQUANT };
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -42,6 +51,7 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if ((uint64_t)N * (uint64_t)row_bytes_of(bits == BQ_BITS_T5 ? BQ_BITS_T5 : 2, K, gs) >= (1ull << 30) ||
       (uint64_t)N * (uint64_t)(K / gs) >= (1ull << 29))
     return BQ_ERR_SHAPE;
+  if (e != E_DEQUANT && e != E_QMM && K / gs > kMaxDecodeGroups) return BQ_ERR_SHAPE;
   if (e != E_DEQUANT) {
     if (M < 1) return BQ_ERR_M;
     if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
@@ -70,8 +80,6 @@ constexpr int kTargetWorkgroups = 256;
 constexpr int kMaxRowsPerWg = 256;
 constexpr size_t kLdsBudget = 150 * 1024;
 
-// 16-byte vectors of a workgroup's scale (or bias) block, at most
-int sb_vectors(int rows_per_wg, int G) { return (int)(((int64_t)rows_per_wg * G * 2 + 15) / 16 + 1); }
 
 size_t qmv_lds_bytes(int M, int rows_per_wg, int ntiles, int seg_tiles, int G) {
   const size_t U = (size_t)((rows_per_wg + kR - 1) / kR) * ntiles;

@@ -40,11 +40,14 @@
  * names it.  A failed launch returns BQ_ERR_HIP.  Nothing aborts or throws
  * across this interface.
  *
- * Alignment: x needs 16-byte alignment (it is read in 16-byte vectors);
- * scales, biases and y need 2-byte alignment, except that bq_dequant with
- * bits 1/2 writes y in 16-byte vectors and needs it 16-byte aligned; w needs
- * 4-byte alignment (uint32 words for bits 1/2; dword loads for t5).  Fresh
- * allocations from hipMalloc or torch meet all of these.  The t5 entry
+ * Alignment: x needs 16-byte alignment (it is read in 16-byte vectors).
+ * The decode calls (qmv, qmv_wide, qmv_sym, t5_qmv, t5_qmv_wide) also read
+ * scales and biases in 16-byte vectors and need them 16-byte aligned
+ * (qmv_sym ignores the bias pointer); bq_t5_qmm and bq_dequant need 2 bytes.
+ * y needs 2-byte alignment, except that bq_dequant with bits 1/2 writes y in
+ * 16-byte vectors and needs it 16-byte aligned; w needs 4-byte alignment
+ * (uint32 words for bits 1/2; dword loads for t5).  Fresh allocations from
+ * hipMalloc or torch meet all of these.  The t5 entry
  * points additionally need K to be a multiple of 256, so that every packed
  * row is a whole number of dwords (true of all the decoder shapes).
  */
@@ -66,7 +69,9 @@ typedef enum bq_status {
   BQ_ERR_GROUP = -3,      /* group_size not 64 or 128 */
   BQ_ERR_SHAPE = -4,      /* N or K not positive, K % group_size != 0, K > 2^26,
                              or N * (packed row bytes) >= 2^30, or
-                             N * (K / group_size) >= 2^29 (32-bit offsets) */
+                             N * (K / group_size) >= 2^29 (32-bit offsets), or
+                             a decode call with K / group_size > 4092 (a
+                             workgroup's scales must fit its LDS) */
   BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
   BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
   BQ_ERR_HIP = -7         /* the HIP runtime rejected a launch */
