@@ -81,67 +81,72 @@ constexpr int kMaxRowsPerWg = 256;
 constexpr size_t kLdsBudget = 150 * 1024;
 
 
-size_t qmv_lds_bytes(int M, int rows_per_wg, int ntiles, int seg_tiles, int G) {
-  const size_t U = (size_t)((rows_per_wg + kR - 1) / kR) * ntiles;
+size_t qmv_lds_bytes(int M, int R, int rows_per_wg, int ntiles, int seg_tiles, int G) {
+  const size_t U = (size_t)((rows_per_wg + R - 1) / R) * ntiles;
   const size_t cs = (size_t)M * kXD + ((M % 2 == 0) ? 4 : 0);
-  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL + 8 * (size_t)sb_vectors(rows_per_wg, G) +
-              U * kR * M);
+  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL +
+              8 * (size_t)sb_entry_dwords(M) * sb_vectors(rows_per_wg, G) + U * R * M);
 }
 
-// Workgroup geometry for M activation rows.  Rows per workgroup: enough for
-// one workgroup per CU.  Segment: as many K tiles of x as LDS and the
-// staging tasks (M * tiles * 16 <= kStageRounds * kThreads) allow, split
-// evenly.  Returns false if even two rows per workgroup do not fit.
-bool qmv_geometry(QmvParams& p, int M) {
+// Workgroup geometry for M activation rows and R rows per unit.  Rows per
+// workgroup: a multiple of R, enough for one workgroup per CU.  Segment: as
+// many K tiles of x as LDS and the staging tasks (M * tiles * 16 <=
+// kStageRounds * kThreads) allow, split evenly.  Returns false if even R rows
+// per workgroup do not fit.
+bool qmv_geometry(QmvParams& p, int M, int R) {
   p.ntiles = (p.K + kTile - 1) / kTile;
   const int max_st = std::min(p.ntiles, kStageRounds * kThreads / (kKL * M));
-  int rows = kR * ((p.N + kR * kTargetWorkgroups - 1) / (kR * kTargetWorkgroups));
+  int rows = R * ((p.N + R * kTargetWorkgroups - 1) / (R * kTargetWorkgroups));
   if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
-  for (; rows >= kR; rows -= kR) {
+  for (; rows >= R; rows -= R) {
     if (sb_vectors(rows, p.G) > kSbRounds * kThreads) continue;
     int st = max_st;
-    while (st > 0 && qmv_lds_bytes(M, rows, p.ntiles, st, p.G) > kLdsBudget) --st;
+    while (st > 0 && qmv_lds_bytes(M, R, rows, p.ntiles, st, p.G) > kLdsBudget) --st;
     if (st == 0) continue;
     p.nseg = (p.ntiles + st - 1) / st;
     p.seg_tiles = (p.ntiles + p.nseg - 1) / p.nseg;
     p.rows_per_wg = rows;
-    p.sb_dwords = 8 * sb_vectors(rows, p.G);
+    p.sb_dwords = 8 * sb_entry_dwords(M) * sb_vectors(rows, p.G);
     return true;
   }
   return false;
 }
 
-// Units each slot keeps in flight: enough to cover a slot's share of a
-// segment where that is small, so that few loads are issued for nothing.
-// The ring depth never changes the arithmetic.
-int units_per_slot(const QmvParams& p) {
-  const int U = ((p.rows_per_wg + kR - 1) / kR) * p.seg_tiles;
+// Units each slot takes in one segment, at most.
+int units_per_slot(const QmvParams& p, int R) {
+  const int U = ((p.rows_per_wg + R - 1) / R) * p.seg_tiles;
   return (U + kSlots - 1) / kSlots;
 }
 
-template <int FMT, int GS, int M, bool IMPLIED, int P>
+template <int FMT, int GS, int M, bool IMPLIED, int P, int R>
 int launch_qmv_p(const QmvParams& p, void* stream) {
-  const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P>);
+  const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P, R>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
   (void)attr;
-  const size_t shmem = qmv_lds_bytes(M, p.rows_per_wg, p.ntiles, p.seg_tiles, p.G);
+  const size_t shmem = qmv_lds_bytes(M, R, p.rows_per_wg, p.ntiles, p.seg_tiles, p.G);
   dim3 grid((p.N + p.rows_per_wg - 1) / p.rows_per_wg);
   QmvParams q = p;
   return launch(fn, grid, dim3(kThreads), shmem, stream, &q);
 }
 
+// Rows per unit R and units in flight per slot P never change a row's
+// arithmetic.  R = 4 halves the per-code share of the per-unit work; it is
+// used for one or two activation rows, where the registers allow it, and
+// where a 4-row workgroup's scale rows fit one staging pass.  A shallow ring
+// is faster: with every slot of the GPU asking for many units at once, HBM
+// returns them in no useful order and each slot waits for its oldest one,
+// and every fetch past a slot's last unit still costs issue slots.
 template <int FMT, int GS, int M, bool IMPLIED>
 int launch_qmv_t(QmvParams p, void* stream) {
-  if (!qmv_geometry(p, M)) return BQ_ERR_SHAPE;
-  if constexpr (M == 1) {
-    const int ups = units_per_slot(p);
-    if (ups <= 2) return launch_qmv_p<FMT, GS, M, IMPLIED, 2>(p, stream);
-    if (ups <= 4) return launch_qmv_p<FMT, GS, M, IMPLIED, 4>(p, stream);
-    return launch_qmv_p<FMT, GS, M, IMPLIED, 6>(p, stream);
-  } else {
-    return launch_qmv_p<FMT, GS, M, IMPLIED, 4>(p, stream);
+  if constexpr (M <= 2) {
+    if (qmv_geometry(p, M, 4)) {
+      if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
+      return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);
+    }
   }
+  if (!qmv_geometry(p, M, 2)) return BQ_ERR_SHAPE;
+  return launch_qmv_p<FMT, GS, M, IMPLIED, 4, 2>(p, stream);
 }
 
 typedef int (*QmvLauncher)(QmvParams, void*);

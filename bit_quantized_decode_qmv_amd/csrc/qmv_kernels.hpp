@@ -59,7 +59,7 @@ constexpr int kKL = 16;            // lanes per slot (chunks per tile)
 constexpr int kWaves = 8;          // waves per workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = kThreads / kKL;
-constexpr int kR = 2;              // rows per row-group
+constexpr int kR = 2;              // rows per row-group, at least (the kernels take R = 2 or 4)
 constexpr int kXD = 36;            // LDS dwords per staged chunk (32-35 used)
 
 struct QmvParams {
@@ -181,6 +181,22 @@ __device__ __forceinline__ float row_sum16(float v) {
   return __builtin_bit_cast(float, x);
 }
 
+// row_sum16 of several values, step by step across all of them, so that no
+// step waits for the one just before it.  Same additions, same order.
+template <int CTL, int N>
+__device__ __forceinline__ void dpp_add_step(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[i]), CTL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ void rows_sum16(float (&v)[N]) {
+  dpp_add_step<0x111>(v);
+  dpp_add_step<0x112>(v);
+  dpp_add_step<0x114>(v);
+  dpp_add_step<0x118>(v);
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
 // global memory, which on this GPU waits for every load in flight (loads and
 // stores share one counter) and would drain the prefetched weights; here only
@@ -195,10 +211,10 @@ __device__ __forceinline__ void lds_barrier() {
 // Forces the partial sums to be computed here: keeps the compiler from
 // sinking the dot products of several quads below later loads, which would
 // keep a whole chunk of x live in registers.
-template <int M>
-__device__ __forceinline__ void pin_partials(float (&Pd)[kR][M]) {
+template <int R, int M>
+__device__ __forceinline__ void pin_partials(float (&Pd)[R][M]) {
 #pragma unroll
-  for (int r = 0; r < kR; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) asm volatile("" : "+v"(Pd[r][m]));
 }
@@ -413,12 +429,17 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
 // --------------------------------------------------------------------------
 // Scale/bias staging.  A workgroup's rows are contiguous in the [N][G] scale
 // and bias arrays, so its block is one byte range; it is read with 16-byte
-// loads from the aligned address at or below its start and stored in LDS as
-// (scale, bias) half pairs, one dword per (row, group), dword 8v+i holding
-// element i of vector v.  Element (row, group) of the block then sits at
-// dword delta + row*G + group, delta = (start mod 16) / 2.
+// loads from the aligned address at or below its start and stored in LDS,
+// one entry per (row, group), entry 8v+i holding element i of vector v.
+// Element (row, group) of the block then sits at entry delta + row*G +
+// group, delta = (start mod 16) / 2.  An entry is a (scale, bias) fp16 pair
+// in one dword, or, for one or two activation rows (where converting per
+// chunk would cost more than the LDS it saves), an fp32 pair whose bias is
+// already -scale * ratio when the bias is implied.
 // --------------------------------------------------------------------------
 constexpr int kSbRounds = 2;  // 16-byte vectors per thread and array
+template <int M> constexpr bool sb_f32() { return M <= 2; }
+constexpr int sb_entry_dwords(int M) { return M <= 2 ? 2 : 1; }
 
 struct SbStage {
   u32x4 s[kSbRounds], b[kSbRounds];
@@ -437,12 +458,26 @@ __device__ __forceinline__ void sbstage_load(rsrc_t rs, rsrc_t rb, uint32_t lo_a
   }
 }
 
-template <bool IMPLIED>
-__device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl) {
+template <bool IMPLIED, bool F32>
+__device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl, float ratio) {
 #pragma unroll
   for (int k = 0; k < kSbRounds; ++k) {
     const int v = (int)threadIdx.x + k * kThreads;
-    if (v < st.nvec) {
+    if (F32 && v < st.nvec) {
+      float o[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sv = st.s[k][j], bv = IMPLIED ? 0u : st.b[k][j];
+        o[4 * j] = lo_half(sv);
+        o[4 * j + 2] = hi_half(sv);
+        o[4 * j + 1] = IMPLIED ? -o[4 * j] * ratio : lo_half(bv);
+        o[4 * j + 3] = IMPLIED ? -o[4 * j + 2] * ratio : hi_half(bv);
+      }
+      float* dst = reinterpret_cast<float*>(sbl) + 16 * v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + 4 * q) = float4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    } else if (!F32 && v < st.nvec) {
       uint32_t o[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -460,9 +495,9 @@ __device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl)
 // Per-chunk multiply: Pd[r][m] = codes(row r) . xstaged(m).
 // xc points at the lane's staged chunk; row m of x is kXD dwords further.
 // --------------------------------------------------------------------------
-template <int FMT, int M>
-__device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint32_t* xc,
-                                          const uint16_t* lut, uint32_t sh, float (&Pd)[kR][M]) {
+template <int FMT, int M, int R>
+__device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint32_t* xc,
+                                          const uint16_t* lut, uint32_t sh, float (&Pd)[R][M]) {
   if constexpr (FMT == FMT_U2 || FMT == FMT_U1) {
     // quad q = 4 staged dwords 4q..4q+3 (2-bit: word q/2, pairs 4(q%2)..;
     // 1-bit: word q/4, pairs 4(q%4)..); the next quad's x is read while
@@ -477,7 +512,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint
         for (int m = 0; m < M; ++m) xb[(q + 1) & 1][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD + 4 * (q + 1));
       }
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
+      for (int r = 0; r < R; ++r) {
         uint32_t c4[4];
         if constexpr (FMT == FMT_U2) {
           const uint32_t wv = wc[r].v[q >> 1];
@@ -510,14 +545,14 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint
           Pd[r][m] = acc;
         }
       }
-      pin_partials<M>(Pd);
+      pin_partials<R, M>(Pd);
     }
   } else {
     // t5: realign each row's 13 bytes (they start `sh` bytes into the first
     // dword), then six byte pairs and the single byte 12 via the table
-    uint32_t rb[kR][4];
+    uint32_t rb[R][4];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         rb[r][j] = __builtin_amdgcn_alignbyte(j < 3 ? wc[r].v[j + 1] : 0u, wc[r].v[j], sh);
@@ -540,7 +575,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint
         }
       }
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
+      for (int r = 0; r < R; ++r) {
         const int t0 = 2 * pr, t1 = 2 * pr + 1;
         const uint32_t b0 = (rb[r][t0 >> 2] >> (8 * (t0 & 3))) & 0xFFu;
         uint32_t v = lut[b0];
@@ -561,7 +596,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint
           Pd[r][m] = acc;
         }
       }
-      pin_partials<M>(Pd);
+      pin_partials<R, M>(Pd);
     }
   }
 }
@@ -569,7 +604,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[kR], const uint
 // --------------------------------------------------------------------------
 // The kernel.
 // --------------------------------------------------------------------------
-template <int FMT, int GS, int M, bool IMPLIED, int P>
+template <int FMT, int GS, int M, bool IMPLIED, int P, int R>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   using F = Fmt<FMT, GS>;
   constexpr int CS = chunk_stride<M>();
@@ -581,15 +616,15 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   uint32_t* xs = smem;                                              // [ST*16][CS]
   float* xsum = reinterpret_cast<float*>(smem + ST * kKL * CS);     // [ST*16][M]
   uint32_t* sbl = reinterpret_cast<uint32_t*>(xsum + ST * kKL * M);  // [sb_dwords]
-  float* part = reinterpret_cast<float*>(sbl + p.sb_dwords);        // [NG*T][kR*M]
+  constexpr bool SBF = sb_f32<M>();
+  float* part = reinterpret_cast<float*>(sbl + p.sb_dwords);        // [NG*T][R*M]
 
   const int tid = threadIdx.x;
   const int slot = tid / kKL;
   const int kl = tid % kKL;
   const int base = blockIdx.x * p.rows_per_wg;
   const int nrow_wg = min(p.rows_per_wg, p.N - base);
-  const int NG = (nrow_wg + kR - 1) / kR;  // row-groups of this workgroup
-  const int nchunks = p.K / 64;
+  const int NG = (nrow_wg + R - 1) / R;  // row-groups of this workgroup
   const uint32_t sh = (uint32_t)(kl & 3);  // t5 run offset inside its first dword
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
@@ -613,29 +648,31 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   sbstage_load<IMPLIED>(make_rsrc(p.s, sb_size), make_rsrc(IMPLIED ? p.s : p.b, sb_size), sb_lo_al, sb_nvec, sbst);
 
   auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
-  // slot k's units of segment s: [lo(k), lo(k+1)) with lo(k) = k*U_s/kSlots
-  auto range_lo_of = [&](int k, int Us) { return (k * Us) / kSlots; };
 
-  // ---- fetch cursor: unit (row-group, tile ft) of the current segment.
+  // ---- Units of segment s: u = g * Ts + t (row-group g, tile t), in the
+  // order of their bytes.  Slot k takes units k, k + kSlots, k + 2 kSlots,
+  // ..., so at every step the workgroup's slots read one contiguous stretch
+  // of its rows.  Cursor step: kSlots units = dg row-groups + dt tiles.
   // Every fetch issues the same loads (rows past N and chunks past K read
   // zeros or data that is never used), so the compiler can wait for exactly
-  // the ring entry it needs.  Fetches past the slot's range use an offset
+  // the ring entry it needs.  Fetches past the last unit use an offset
   // outside every buffer: no memory is touched and zeros come back.
-  Chunk<FMT> ring[P][kR];
-  int fTs = 1, ft = 0, fleft = 0;
-  uint32_t fwrow = 0, fc0 = 0, fc = 0;
+  Chunk<FMT> ring[P][R];
+  int fTs = 1, fdg = 0, fdt = 0, ft = 0, fleft = 0;
+  uint32_t fwrow = 0, fc0 = 0;
   auto fetch_start = [&](int s) {
     fTs = seg_tiles(s);
-    const int Us = NG * fTs;
-    const int a = range_lo_of(slot, Us);
-    const int g = a / fTs;
-    ft = a - g * fTs;
-    fleft = range_lo_of(slot + 1, Us) - a;
-    fwrow = (uint32_t)(base + g * kR) * (uint32_t)p.row_bytes;
+    fdg = kSlots / fTs;
+    fdt = kSlots - fdg * fTs;
+    const int g = slot / fTs;
+    ft = slot - g * fTs;
+    const int U = NG * fTs;
+    fleft = slot < U ? (U - 1 - slot) / kSlots + 1 : 0;
+    fwrow = (uint32_t)(base + g * R) * (uint32_t)p.row_bytes;
     fc0 = (uint32_t)(s * ST * kKL + kl);
-    fc = fc0 + (uint32_t)(ft * kKL);
   };
-  auto fetch = [&](Chunk<FMT>(&dst)[kR]) {
+  auto fetch = [&](Chunk<FMT>(&dst)[R]) {
+    const uint32_t fc = fc0 + (uint32_t)(ft * kKL);
     const bool live = fleft > 0;
     // buffers are below 2^30 bytes: bit 31 puts a dead fetch out of range
     const uint32_t dead = live ? 0u : 0x80000000u;
@@ -643,83 +680,103 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
     // don't-care register that may still be the target of a load in flight
     const uint32_t wo = fwrow + __umul24(fc, (uint32_t)F::CB);
 #pragma unroll
-    for (int r = 0; r < kR; ++r) load_chunk<FMT>(dst[r], rw, (wo + (uint32_t)(r * p.row_bytes)) | dead);
+    for (int r = 0; r < R; ++r) load_chunk<FMT>(dst[r], rw, (wo + (uint32_t)(r * p.row_bytes)) | dead);
     if (live) {
       --fleft;
-      fc += kKL;
-      if (++ft == fTs) {
-        ft = 0;
-        fc = fc0;
-        fwrow += kR * (uint32_t)p.row_bytes;
+      ft += fdt;
+      int dg = fdg;
+      if (ft >= fTs) {
+        ft -= fTs;
+        ++dg;
       }
+      fwrow += (uint32_t)(dg * R) * (uint32_t)p.row_bytes;
     }
   };
 
   // Each unit's partial products, summed over the slot's 16 lanes, go to
-  // part[(row-group * T + tile) * kR*M + r*M + m]; rows then add their tiles
+  // part[(row-group * T + tile) * R*M + r*M + m]; rows then add their tiles
   // in order.  No sum depends on M, on the segment length or on which slot
   // took the unit, so a row's result is the same in every such launch.
-  int cg = 0, ct = 0;  // compute cursor (row-group, tile within the segment)
-  auto process = [&](int s, int Ts, const Chunk<FMT>(&wc)[kR]) {
+  int cg = 0, ct = 0, cdg = 0, cdt = 0, cTs = 1;  // compute cursor, same steps
+  auto process = [&](int s, const Chunk<FMT>(&wc)[R]) {
     const int cs = ct * kKL + kl;  // chunk within the staged segment
     const int tile = s * ST + ct;
     const int chunk = tile * kKL + kl;
-    const bool valid = chunk < nchunks;
-    // (scale, bias) of both rows; chunks past K read the row's last group,
-    // unused
+    // (scale, bias) of the unit's rows.  A chunk past K reads its row's last
+    // group; its staged x and x sum are zero, so it adds exactly 0.
     const int grp = min((chunk * 64) / GS, p.G - 1);
-    uint32_t sbv[kR];
+    float sc[R], bb[R];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) sbv[r] = sbl[sb_delta + (cg * kR + r) * p.G + grp];
-    float Pd[kR][M];
+    for (int r = 0; r < R; ++r) {
+      const int e = sb_delta + (cg * R + r) * p.G + grp;
+      if constexpr (SBF) {
+        const float2 v = *reinterpret_cast<const float2*>(sbl + 2 * e);
+        sc[r] = v.x;
+        bb[r] = v.y;
+      } else {
+        const uint32_t v = sbl[e];
+        sc[r] = lo_half(v);
+        bb[r] = IMPLIED ? -sc[r] * p.ratio : hi_half(v);
+      }
+    }
+    float Pd[R][M];
 #pragma unroll
-    for (int r = 0; r < kR; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) Pd[r][m] = 0.f;
-    chunk_dot<FMT, M>(wc, xs + cs * CS, lut, sh, Pd);
+    chunk_dot<FMT, M, R>(wc, xs + cs * CS, lut, sh, Pd);
     float X[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) X[m] = xsum[cs * M + m];
-    float* dst = part + (cg * T + tile) * (kR * M);
+    float v[R * M];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      // a chunk past K contributes 0
-      const float sc = valid ? lo_half(sbv[r]) : 0.f;
-      const float bb = IMPLIED ? -sc * p.ratio : (valid ? hi_half(sbv[r]) : 0.f);
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float v = row_sum16(__builtin_fmaf(bb, X[m], sc * Pd[r][m]));
-        if (kl == kKL - 1) dst[r * M + m] = v;
-      }
+      for (int m = 0; m < M; ++m) v[r * M + m] = __builtin_fmaf(bb[r], X[m], sc[r] * Pd[r][m]);
+    rows_sum16<R * M>(v);
+    if (kl == kKL - 1) {
+      float* dst = part + (cg * T + tile) * (R * M);
+#pragma unroll
+      for (int i = 0; i < R * M; ++i) dst[i] = v[i];
     }
-    if (++ct == Ts) {
-      ct = 0;
+    ct += cdt;
+    cg += cdg;
+    if (ct >= cTs) {
+      ct -= cTs;
       ++cg;
     }
   };
 
-  // ring fill for segment 0 (after the x loads); a slot without units
-  // fetches nothing
+  // Ring fill for segment 0.  Only kEarly units per slot go out before the
+  // staging barrier: the x and scale loads share the memory queues with the
+  // weight loads, and every weight byte requested ahead of them delays the
+  // start of the arithmetic.  A slot without units fetches nothing.
+  constexpr int kEarly = P < 1 ? P : 1;
   fetch_start(0);
 #pragma unroll
-  for (int j = 0; j < P; ++j) fetch(ring[j]);
+  for (int j = 0; j < kEarly; ++j) fetch(ring[j]);
   if constexpr (FMT == FMT_T5) {
     if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
   }
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
-  sbstage_commit<IMPLIED>(sbst, sbl);
+  sbstage_commit<IMPLIED, SBF>(sbst, sbl, p.ratio);
   lds_barrier();  // x of segment 0, scales and biases staged; table built
+#pragma unroll
+  for (int j = kEarly; j < P; ++j) fetch(ring[j]);
 
   for (int s = 0; s < p.nseg; ++s) {
-    const int Ts = seg_tiles(s);
-    const int a = range_lo_of(slot, NG * Ts), b = range_lo_of(slot + 1, NG * Ts);
-    cg = a / Ts;
-    ct = a - cg * Ts;
-    for (int i = a; i < b; i += P) {
+    cTs = seg_tiles(s);
+    cdg = kSlots / cTs;
+    cdt = kSlots - cdg * cTs;
+    cg = slot / cTs;
+    ct = slot - cg * cTs;
+    const int U = NG * cTs;
+    const int n = slot < U ? (U - 1 - slot) / kSlots + 1 : 0;  // units of this slot
+    for (int i = 0; i < n; i += P) {
 #pragma unroll
       for (int j = 0; j < P; ++j) {
-        if (i + j < b) process(s, Ts, ring[j]);
+        if (i + j < n) process(s, ring[j]);
         fetch(ring[j]);
       }
     }
@@ -740,15 +797,15 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   }
 
   // y = sum over the row's tiles, in tile order, * 2^24
-  for (int idx = tid; idx < NG * kR * M; idx += kThreads) {
-    const int g = idx / (kR * M);
-    const int rm = idx - g * (kR * M);
+  for (int idx = tid; idx < NG * R * M; idx += kThreads) {
+    const int g = idx / (R * M);
+    const int rm = idx - g * (R * M);
     const int r = rm / M, m = rm - r * M;
-    if (g * kR + r >= nrow_wg) continue;
-    const float* src = part + g * T * (kR * M) + rm;
+    if (g * R + r >= nrow_wg) continue;
+    const float* src = part + g * T * (R * M) + rm;
     float v = 0.f;
-    for (int t = 0; t < T; ++t) v += src[t * (kR * M)];
-    p.y[(size_t)m * p.N + base + g * kR + r] = (half_t)(v * 16777216.0f);
+    for (int t = 0; t < T; ++t) v += src[t * (R * M)];
+    p.y[(size_t)m * p.N + base + g * R + r] = (half_t)(v * 16777216.0f);
   }
 }
 
