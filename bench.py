@@ -5,8 +5,10 @@ Workload (one step): the decode QMV of one hidden=5120 decoder layer at M=1
 -- the seven projection shapes (q 6144x5120, k/v 1024x5120, o 5120x6144,
 gate/up 17408x5120, down 5120x17408) -- for bits 1 and 2 and group sizes 64
 and 128 (28 calls, affine weights with stored biases).  Inputs are seeded
-synthetic tensors already resident in HBM; two distinct copies alternate
-between steps so that the 256 MB last-level cache cannot serve the weights.
+synthetic tensors already resident in HBM.  Every timed sequence rotates
+through enough distinct copies of its inputs (at least 512 MB) that the
+256 MB last-level cache cannot serve the weights from one launch to the
+next.
 
 value = algorithmic bytes of a step (packed W + scales + biases + x + y)
         / measured step time, in GB/s.
@@ -17,7 +19,15 @@ launch overhead from Python is not in the timed region.
 Extra objects on the JSON line:
   roofline      the dominant kernel (2-bit, gs=64, M=1) over its seven shapes:
                 algorithmic bytes per launch / average launch duration from
-                HIP events around graph replays of just those launches.
+                HIP events around graph replays of just those launches (the
+                duration is the launch period in the graph: kernel time plus
+                the gap to the next launch).  traffic: HBM bytes per launch
+                from FETCH_SIZE + WRITE_SIZE counters, calibrated on a copy
+                kernel, when taken on the current kernel sources.
+
+Counter runs (under rocprofv3 --pmc, one counter per run):
+  python3 bench.py --counters              calibration copy + cold launches
+  python3 bench.py --traffic-from F.csv W.csv   writes profiles/traffic.json
   cpu_baseline  the fp64 CPU oracle on a bounded sample (see --cpu-sample).
   breakdown     per (bits, gs, shape) microseconds and GB/s.
 """
@@ -37,6 +47,13 @@ if ROOT not in sys.path:
 METRIC = "QMV achieved HBM GB/s (W+scales+biases+x) at M=1..5; % of MI355X peak"
 PEAK_HBM_GBS = 8000.0
 SHAPES = ("q", "k", "v", "o", "gate", "up", "down")
+COLD_BYTES = 512 << 20  # rotation set: twice the last-level cache
+CAL_BYTES = 256 << 20   # calibration copy: bytes read and bytes written
+DOMINANT = "qmv_u2_gs64_m1"
+
+
+def n_copies(bytes_per_copy):
+    return max(2, -(-COLD_BYTES // max(1, bytes_per_copy)))
 
 
 def parse():
@@ -50,6 +67,12 @@ def parse():
     ap.add_argument("--suite", default="", help="'full': also time M=1..5 wide/sym, t5 and qmm "
                     "configurations and write them to --detail-csv")
     ap.add_argument("--detail-csv", default=os.path.join(ROOT, "gpurun_out", "bench_detail.csv"))
+    ap.add_argument("--counters", action="store_true",
+                    help="eager calibration copy and one cold launch per shape of the dominant kernel, for "
+                         "rocprofv3 --pmc runs")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="rocprofv3 counter_collection.csv files of --counters runs with FETCH_SIZE and "
+                         "WRITE_SIZE; writes profiles/traffic.json")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + steps only (for rocprofv3), skip the extra measurements")
     return ap.parse_args()
@@ -93,18 +116,22 @@ def upload(torch, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def make_calls(torch, dev, specs, copies):
+def make_calls(torch, dev, specs, copies=None):
     """specs: list of (entry, fmt, M, N, K, gs, variant, label).  Returns
-    calls[copy][i] with distinct device buffers per copy."""
+    calls[copy][i] with distinct device buffers per copy; by default as many
+    copies as it takes for all of them to fill COLD_BYTES."""
     import synth
-    out = [[] for _ in range(copies)]
+    base = []
     for (entry, fmt, M, N, K, gs, variant, label) in specs:
         inp = synth.make_inputs(fmt, M, N, K, gs, variant, seed=0)
+        base.append([upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)])
+    if copies is None:
+        per_copy = sum(sum(t.numel() * t.element_size() for t in ts if t is not None) for ts in base)
+        copies = n_copies(per_copy)
+    out = [[] for _ in range(copies)]
+    for (entry, fmt, M, N, K, gs, variant, label), ts in zip(specs, base):
         for c in range(copies):
-            x = upload(torch, inp.x, dev)
-            w = upload(torch, inp.w, dev)
-            s = upload(torch, inp.scales, dev)
-            b = upload(torch, inp.biases, dev)
+            x, w, s, b = [t if (c == 0 or t is None) else t.clone() for t in ts]
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             out[c].append(Call(entry, fmt, M, N, K, gs, (x, w, s, b, y), label))
     return out
@@ -133,8 +160,10 @@ def time_graphs(torch, graphs, replays):
 
 
 def per_call_seconds(torch, lib, call_copies, launches=40, replays=5):
-    """Average duration of one call: graph of `launches` back-to-back launches
-    alternating between buffer copies, replayed `replays` times."""
+    """Average duration of one call: graph of back-to-back launches rotating
+    through the buffer copies (at least `launches`, at least one pass over
+    the copies), replayed `replays` times."""
+    launches = max(launches, len(call_copies))
     seq = [call_copies[i % len(call_copies)] for i in range(launches)]
     g = capture(torch, lib, seq)
     g.replay()
@@ -224,8 +253,8 @@ def full_suite(torch, lib, dev, path):
     with open(path, "w") as f:
         f.write("entry,fmt,variant,M,shape,N,K,gs,us,GBps,frac_hbm,TFLOPs\n")
         for spec in specs + qmm_specs:
-            copies = make_calls(torch, dev, [spec], 2)
-            pair = [copies[0][0], copies[1][0]]
+            copies = make_calls(torch, dev, [spec])
+            pair = [cs[0] for cs in copies]
             launches = 8 if spec[0] == "bq_t5_qmm" and spec[2] >= 512 else 40
             t = per_call_seconds(torch, lib, pair, launches=launches, replays=3)
             c = pair[0]
@@ -242,8 +271,86 @@ def full_suite(torch, lib, dev, path):
     return rows
 
 
+def counter_run(torch, lib, dev):
+    """Eager launches for counter runs: one calibration copy kernel of
+    CAL_BYTES read and CAL_BYTES written, then each shape of the dominant
+    kernel once, each after a fresh pass of the calibration copy so that its
+    inputs come from HBM."""
+    import synth
+    src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    torch.add(src, 1.0, out=dst)  # calibration: reads and writes CAL_BYTES
+    torch.cuda.synchronize()
+    specs = []
+    for shape in SHAPES:
+        N, K = synth.PROJECTION_SHAPES[shape]
+        specs.append(("bq_qmv", "u2", 1, N, K, 64, "asym", f"u2/gs64/{shape}"))
+    calls = make_calls(torch, dev, specs, copies=1)[0]
+    h = torch.cuda.current_stream().cuda_stream
+    for c in calls:
+        torch.add(dst, 1.0, out=src)  # evicts the last-level cache
+        torch.cuda.synchronize()
+        c.launch(lib, h)
+        torch.cuda.synchronize()
+    print(json.dumps({"counter_run": [c.label for c in calls], "bytes": [c.bytes for c in calls]}), flush=True)
+
+
+def traffic_from(fetch_csv, write_csv):
+    """profiles/traffic.json from the counter_collection.csv files of two
+    --counters runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)."""
+    import csv
+
+    def read(path, counter):
+        rows = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return rows
+
+    out = {}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = read(path, counter)
+        # the calibration copy: the first elementwise add (not the fill that made its input)
+        cal = [v for (_, name, v) in rows if "elementwise" in name and "_add" in name]
+        qmv = [v for (_, name, v) in rows if "qmv_kernel<2, 64, 1, false" in name]
+        if not cal or len(qmv) != len(SHAPES):
+            raise SystemExit(f"{path}: expected a calibration copy and {len(SHAPES)} qmv dispatches, "
+                             f"found {len(cal)} and {len(qmv)}")
+        factor = cal[0] * 1024.0 / CAL_BYTES  # counter KiB per true KiB
+        per[counter] = [v * 1024.0 / factor for v in qmv]
+        out[counter] = {"calibration_kib": cal[0], "factor": round(factor, 4),
+                        "kib_per_dispatch": [round(v, 1) for v in qmv]}
+    per_launch = [f + w for f, w in zip(per["FETCH_SIZE"], per["WRITE_SIZE"])]
+    import synth
+    alg = [algorithmic_bytes("u2", 1, *synth.PROJECTION_SHAPES[s], 64, True) for s in SHAPES]
+    rec = {
+        "source_hash": kernel_source_hash(),
+        "shapes": list(SHAPES),
+        "bytes_per_launch": int(sum(per_launch) / len(per_launch)),
+        "algorithmic_bytes_per_launch": int(sum(alg) / len(alg)),
+        "per_shape_bytes": [int(v) for v in per_launch],
+        "per_shape_algorithmic_bytes": alg,
+        "counters": out,
+        "method": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, on python3 bench.py --counters; each divided "
+                  f"by what it reads for a copy of {CAL_BYTES >> 20} MiB read + {CAL_BYTES >> 20} MiB written",
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[DOMINANT] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the QMV path has no multi-GPU mode in this build "
@@ -261,6 +368,9 @@ def main():
     lib = bq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.counters:
+        counter_run(torch, lib, dev)
+        return
 
     specs = []
     for bits in (1, 2):
@@ -269,8 +379,8 @@ def main():
             for shape in SHAPES:
                 N, K = synth.PROJECTION_SHAPES[shape]
                 specs.append(("bq_qmv", fmt, 1, N, K, gs, "asym", f"{fmt}/gs{gs}/{shape}"))
-    print(f"bench: generating {len(specs)} calls x 2 copies", file=sys.stderr, flush=True)
-    copies = make_calls(torch, dev, specs, 2)
+    copies = make_calls(torch, dev, specs)
+    print(f"bench: {len(specs)} calls x {len(copies)} copies", file=sys.stderr, flush=True)
     step_bytes = sum(c.bytes for c in copies[0])
 
     # eager warm-up (loads the code object before any capture)
@@ -282,7 +392,7 @@ def main():
 
     graphs = [capture(torch, lib, cs) for cs in copies]
     for i in range(args.warmup):
-        graphs[i % 2].replay()
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
     elapsed = time_graphs(torch, graphs, args.steps)
@@ -314,18 +424,17 @@ def main():
 
     if not args.profile_only:
         # dominant kernel: 2-bit, gs=64, M=1 affine, over its seven shapes
-        dom = [i for i, c in enumerate(copies[0]) if c.fmt == "u2" and c.gs == 64]
-        seq = []
-        for rep in range(4):
-            for i in dom:
-                seq.append(copies[rep % 2][i])
+        dom_specs = [sp for sp in specs if sp[1] == "u2" and sp[5] == 64]
+        dom_copies = make_calls(torch, dev, dom_specs)
+        seq = [c for cs in dom_copies for c in cs]
         gd = capture(torch, lib, seq)
         gd.replay()
-        reps = 10
+        reps = 5
         t = time_graphs(torch, [gd], reps)
         avg_launch = t / (reps * len(seq))
-        bytes_per_launch = sum(copies[0][i].bytes for i in dom) / len(dom)
+        bytes_per_launch = sum(c.bytes for c in dom_copies[0]) / len(dom_copies[0])
         achieved = bytes_per_launch / avg_launch / 1e9
+        del gd, dom_copies, seq
         result["roofline"] = {
             "bound": "hbm",
             "kernel": "qmv_kernel<2-bit, gs=64, M=1, stored bias>",
@@ -333,18 +442,22 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic("qmv_u2_gs64_m1"),
+            "traffic": measured_traffic(DOMINANT),
             "avg_launch_us": round(avg_launch * 1e6, 3),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
         }
         bd = {}
-        for i, c in enumerate(copies[0]):
-            ts = per_call_seconds(torch, lib, [copies[0][i], copies[1][i]], launches=20, replays=3)
+        for spec in specs:
+            cc = make_calls(torch, dev, [spec])
+            ts = per_call_seconds(torch, lib, [cs[0] for cs in cc], launches=20, replays=3)
+            c = cc[0][0]
             bd[c.label] = {"us": round(ts * 1e6, 2), "GBps": round(c.bytes / ts / 1e9, 1)}
+            del cc
         result["breakdown"] = bd
         if args.suite == "full":
             os.makedirs(os.path.dirname(args.detail_csv), exist_ok=True)
-            del graphs, gd
+            del graphs
+            torch.cuda.empty_cache()
             full_suite(torch, lib, dev, args.detail_csv)
         if not args.no_cpu_baseline:
             shapes = [s for s in args.cpu_sample.split(",") if s]
