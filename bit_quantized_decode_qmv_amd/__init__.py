@@ -9,8 +9,10 @@ Two layers:
 * ``bq_*`` functions with the C names and C arguments (integers for
   pointers and the stream); they raise :class:`BQError` on a nonzero status.
 * tensor helpers (``qmv``, ``qmv_wide``, ``qmv_sym``, ``t5_qmv``,
-  ``t5_qmv_wide``, ``t5_qmm``, ``dequant``) that check devices, dtypes and
-  contiguity, allocate the output and pass the current stream.
+  ``t5_qmv_wide``, ``t5_qmm``, ``dequant``, ``linear``, ``sym_check``) that
+  check devices, dtypes and contiguity, allocate the output and pass the
+  current stream, and :class:`QuantizedWeight`, a layer's packed weights
+  with its symmetric-bias check done once.
 
 The library is loaded on first use; a missing build or an ABI mismatch is an
 error (there is no fallback path).
@@ -21,20 +23,24 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 BITS_T5 = 0
 MAX_WIDE_M = 5
+LINEAR_SYM = 1
+T5_QMM_MIN_M = 17
+ROUTES = {1: "qmv_wide", 2: "qmv_sym", 3: "t5_qmv_wide", 4: "t5_qmm"}
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
                 "bq_t5_qmm", "bq_dequant")
-ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS
+DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check")
+ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
 
 STATUS = {
     0: "BQ_OK", -1: "BQ_ERR_NULL", -2: "BQ_ERR_BITS", -3: "BQ_ERR_GROUP", -4: "BQ_ERR_SHAPE",
-    -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP",
+    -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP", -8: "BQ_ERR_FLAGS",
 }
 
 
@@ -66,6 +72,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.bq_linear.restype = ctypes.c_int
+    lib.bq_linear.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.bq_linear_route.restype = ctypes.c_int
+    lib.bq_linear_route.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.bq_sym_check.restype = ctypes.c_int
+    lib.bq_sym_check.argtypes = [vp, vp, i, i, i, i, vp, vp]
     ver = lib.bq_abi_version()
     if ver != ABI_VERSION:
         raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
@@ -105,6 +117,31 @@ bq_dequant = _c_entry("bq_dequant")
 
 def bq_abi_version() -> int:
     return load_library().bq_abi_version()
+
+
+def _raise_if(st: int, name: str) -> int:
+    if st < 0:
+        raise BQError(st, load_library().bq_strerror(st).decode(), name)
+    return st
+
+
+def bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags, stream=None):
+    """C entry point bq_linear of include/bq.h (pointers and stream as integers)."""
+    return _raise_if(load_library().bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags,
+                                               stream), "bq_linear")
+
+
+def bq_linear_route(M, bits, flags=0):
+    """(route name, passes) bq_linear takes for (M, bits, flags); host only."""
+    passes = ctypes.c_int(0)
+    st = _raise_if(load_library().bq_linear_route(M, bits, flags, ctypes.byref(passes)), "bq_linear_route")
+    return ROUTES[st], passes.value
+
+
+def bq_sym_check(scales, biases, N, K, bits, group_size, flag, stream=None):
+    """C entry point bq_sym_check of include/bq.h (flag: device int pointer)."""
+    return _raise_if(load_library().bq_sym_check(scales, biases, N, K, bits, group_size, flag, stream),
+                     "bq_sym_check")
 
 
 # ---------------------------------------------------------------------------
@@ -205,9 +242,73 @@ def dequant(w, scales, biases, bits: int, group_size: int, K: int, out=None):
     return _run("bq_dequant", None, w, scales, biases, bits, group_size, out, 0, N, K, (N, K))
 
 
+def sym_check(scales, biases, bits: int, group_size: int) -> bool:
+    """True when every bias equals -scale*ratio exactly (ratio (2^bits-1)/2,
+    t5: 1), checked on the GPU; waits for the result."""
+    torch = _torch()
+    dev = scales.device
+    _check(scales, "scales", torch.float16, dev)
+    _check(biases, "biases", torch.float16, dev)
+    if tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("scales and biases must have the same shape")
+    N, G = scales.shape
+    flag = torch.empty(1, dtype=torch.int32, device=dev)
+    bq_sym_check(scales.data_ptr(), biases.data_ptr(), N, G * group_size, bits, group_size, flag.data_ptr(),
+                 _stream_handle(dev))
+    return bool(flag.item())
+
+
+class QuantizedWeight:
+    """One layer's packed weights: w (int32 words for bits 1/2, uint8 t5
+    bytes), fp16 scales [N][K/gs], fp16 biases or None (implied bias).  The
+    symmetric-bias check runs once, on first use."""
+
+    def __init__(self, w, scales, biases, bits: int, group_size: int):
+        self.w, self.scales, self.biases = w, scales, biases
+        self.bits, self.group_size = bits, group_size
+        self.N = scales.shape[0]
+        self.K = scales.shape[1] * group_size
+        self._sym = None if biases is not None else True
+
+    @property
+    def sym(self) -> bool:
+        if self._sym is None:
+            self._sym = sym_check(self.scales, self.biases, self.bits, self.group_size)
+        return self._sym
+
+
+def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
+    """y = x . W^T for any number of rows, routed as bq_linear does (bits
+    1/2: passes of up to 5 rows through the wide or symmetric kernel; t5:
+    wide passes below T5_QMM_MIN_M rows, the fused qmm from there).  sym
+    defaults to the layer's checked symmetric-bias property."""
+    use_sym = qw.sym if sym is None else sym
+    M, K = x.shape
+    if K != qw.K:
+        raise ValueError(f"x has K = {K}, the weight {qw.K}")
+    torch = _torch()
+    dev = qw.w.device
+    _check(qw.w, "w", torch.uint8 if qw.bits == BITS_T5 else torch.int32, dev)
+    _check(qw.scales, "scales", torch.float16, dev)
+    if qw.biases is not None:
+        _check(qw.biases, "biases", torch.float16, dev)
+    _check(x, "x", torch.float16, dev)
+    if out is None:
+        out = torch.empty((M, qw.N), dtype=torch.float16, device=dev)
+    else:
+        _check(out, "out", torch.float16, dev)
+        if tuple(out.shape) != (M, qw.N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, qw.N)}")
+    bq_linear(x.data_ptr(), qw.w.data_ptr(), qw.scales.data_ptr(),
+              qw.biases.data_ptr() if qw.biases is not None else None, out.data_ptr(), M, qw.N, qw.K, qw.bits,
+              qw.group_size, LINEAR_SYM if use_sym else 0, _stream_handle(dev))
+    return out
+
+
 __all__ = [
-    "ABI_VERSION", "ALL_SYMBOLS", "BITS_T5", "BQError", "ENTRY_POINTS", "LIB_PATH", "MAX_WIDE_M",
-    "bq_abi_version", "bq_dequant", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_t5_qmm",
-    "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "load_library", "qmv", "qmv_sym", "qmv_wide",
-    "strerror", "t5_qmm", "t5_qmv", "t5_qmv_wide",
+    "ABI_VERSION", "ALL_SYMBOLS", "BITS_T5", "BQError", "DISPATCH_POINTS", "ENTRY_POINTS", "LIB_PATH",
+    "LINEAR_SYM", "MAX_WIDE_M", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
+    "bq_linear", "bq_linear_route", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
+    "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmv", "qmv_sym", "qmv_wide",
+    "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide",
 ]

@@ -9,6 +9,7 @@
 #include "dequant_kernels.hpp"
 #include "qmm_kernels.hpp"
 #include "qmv_kernels.hpp"
+#include "sym_kernels.hpp"
 
 namespace {
 
@@ -222,11 +223,13 @@ const char* bq_strerror(int status) {
     case BQ_ERR_NULL: return "a required pointer is NULL";
     case BQ_ERR_BITS: return "bits is not valid for this entry point (1, 2, or BQ_BITS_T5 = 0)";
     case BQ_ERR_GROUP: return "group_size must be 64 or 128";
-    case BQ_ERR_SHAPE: return "N and K must be positive, K a multiple of group_size and at most 2^30";
+    case BQ_ERR_SHAPE:
+      return "N and K must be positive, K a multiple of group_size, and the sizes within the limits of bq.h";
     case BQ_ERR_M: return "M is outside the range this entry point accepts";
     case BQ_ERR_ALIGN:
       return "a pointer is misaligned (x, and for the decode calls scales and biases, need 16 bytes), or a t5 "
              "call has K not a multiple of 256";
+    case BQ_ERR_FLAGS: return "flags holds bits this entry point does not define";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
   }
   return "unknown bq status";
@@ -313,6 +316,62 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
   const size_t blocks = (items + 255) / 256;
   if (blocks > 0x7FFFFFFF) return BQ_ERR_SHAPE;
   return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
+}
+
+int bq_linear_route(int M, int bits, int flags, int* passes) {
+  if (M < 1) return BQ_ERR_M;
+  if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
+  int route, n;
+  if (bits == BQ_BITS_T5 && M >= BQ_T5_QMM_MIN_M) {
+    route = BQ_ROUTE_T5_QMM;
+    n = 1;
+  } else {
+    route = bits == BQ_BITS_T5 ? BQ_ROUTE_T5_WIDE : ((flags & BQ_LINEAR_SYM) ? BQ_ROUTE_QMV_SYM : BQ_ROUTE_QMV_WIDE);
+    n = (M + BQ_MAX_WIDE_M - 1) / BQ_MAX_WIDE_M;
+  }
+  if (passes) *passes = n;
+  return route;
+}
+
+int bq_linear(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
+              int K, int bits, int group_size, int flags, void* stream) {
+  if ((flags & ~BQ_LINEAR_SYM) != 0) return BQ_ERR_FLAGS;
+  int passes = 0;
+  const int route = bq_linear_route(M, bits, flags, &passes);
+  if (route < 0) return route;
+  // symmetric: the bias is implied and never read (t5: -scale)
+  const void* b = (flags & BQ_LINEAR_SYM) ? nullptr : biases;
+  if (route == BQ_ROUTE_T5_QMM) return bq_t5_qmm(x, w, scales, b, y, M, N, K, bits, group_size, stream);
+  const Entry e = route == BQ_ROUTE_T5_WIDE ? E_T5_WIDE : (route == BQ_ROUTE_QMV_SYM ? E_SYM : E_WIDE);
+  // every pass is validated in full before it launches; the first check
+  // also covers the arguments common to all passes
+  for (int m0 = 0; m0 < M; m0 += BQ_MAX_WIDE_M) {
+    const int mc = M - m0 < BQ_MAX_WIDE_M ? M - m0 : BQ_MAX_WIDE_M;
+    const void* xm = x ? static_cast<const void*>(static_cast<const half_t*>(x) + (size_t)m0 * K) : nullptr;
+    void* ym = y ? static_cast<void*>(static_cast<half_t*>(y) + (size_t)m0 * N) : nullptr;
+    const int st = run_qmv(e, xm, w, scales, b, ym, mc, N, K, bits, group_size, stream);
+    if (st != BQ_OK) return st;
+  }
+  return BQ_OK;
+}
+
+int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits, int group_size, int* flag,
+                 void* stream) {
+  if (!scales || !biases || !flag) return BQ_ERR_NULL;
+  if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
+  if (group_size != 64 && group_size != 128) return BQ_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % group_size != 0) return BQ_ERR_SHAPE;
+  if (!aligned(scales, 2) || !aligned(biases, 2) || !aligned(flag, 4)) return BQ_ERR_ALIGN;
+  SymCheckParams p{};
+  p.s = static_cast<const _Float16*>(scales);
+  p.b = static_cast<const _Float16*>(biases);
+  p.n = (int64_t)N * (K / group_size);
+  p.ratio = bits == BQ_BITS_T5 ? 1.0f : (bits == 1 ? 0.5f : 1.5f);
+  p.flag = flag;
+  int st = launch(reinterpret_cast<const void*>(&sym_flag_init_kernel), dim3(1), dim3(64), 0, stream, &p);
+  if (st != BQ_OK) return st;
+  const int64_t blocks = std::min<int64_t>((p.n + 255) / 256, 2048);
+  return launch(reinterpret_cast<const void*>(&sym_check_kernel), dim3((unsigned)blocks), dim3(256), 0, stream, &p);
 }
 
 }  // extern "C"

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 1
+#define BQ_ABI_VERSION 2
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -74,8 +74,21 @@ typedef enum bq_status {
                              workgroup's scales must fit its LDS) */
   BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
   BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
-  BQ_ERR_HIP = -7         /* the HIP runtime rejected a launch */
+  BQ_ERR_HIP = -7,        /* the HIP runtime rejected a launch */
+  BQ_ERR_FLAGS = -8       /* bq_linear: flags holds undefined bits */
 } bq_status;
+
+/* bq_linear flags */
+#define BQ_LINEAR_SYM 1   /* bias implied (-scale*ratio; t5: -scale), biases never read */
+/* t5 calls of bq_linear with M >= BQ_T5_QMM_MIN_M take the fused qmm path */
+#define BQ_T5_QMM_MIN_M 17
+
+typedef enum bq_route {
+  BQ_ROUTE_QMV_WIDE = 1,  /* bits 1/2, stored bias: bq_qmv_wide per pass of <= 5 rows */
+  BQ_ROUTE_QMV_SYM = 2,   /* bits 1/2, implied bias: bq_qmv_sym per pass of <= 5 rows */
+  BQ_ROUTE_T5_WIDE = 3,   /* t5: bq_t5_qmv_wide per pass of <= 5 rows */
+  BQ_ROUTE_T5_QMM = 4     /* t5, M >= BQ_T5_QMM_MIN_M: one bq_t5_qmm */
+} bq_route;
 
 /* ABI version of the loaded library; callers must refuse to use a library
  * whose version differs from BQ_ABI_VERSION (the probe of section 三, but a
@@ -129,6 +142,39 @@ int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* bias
  * for bits 1/2 and -scale for t5. */
 int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y,
                int M, int N, int K, int bits, int group_size, void* stream);
+
+/* linear -- the routing of section 二 (the kernels are chosen by bits and
+ * by the number of activation rows M) and section 三 (1/2-bit affine layers
+ * in decode take the fast kernels): y = x * W^T for any M >= 1.
+ *   bits 1/2: passes of up to 5 rows through bq_qmv_wide, or bq_qmv_sym when
+ *             flags has BQ_LINEAR_SYM (each pass reads W once; M > 5 reads it
+ *             ceil(M/5) times);
+ *   t5:       M < BQ_T5_QMM_MIN_M: passes of up to 5 rows through
+ *             bq_t5_qmv_wide; M >= BQ_T5_QMM_MIN_M: bq_t5_qmm (the
+ *             article's prefill rule, M > 16).
+ * Arguments as for the entry point a pass goes to; with BQ_LINEAR_SYM the
+ * biases argument is ignored (may be NULL).  Results are those of the
+ * entry points the passes take; each pass is validated before it launches,
+ * so an invalid argument fails before anything runs.  Undefined flag bits:
+ * BQ_ERR_FLAGS. */
+int bq_linear(const void* x, const void* w, const void* scales, const void* biases, void* y,
+              int M, int N, int K, int bits, int group_size, int flags, void* stream);
+
+/* The route bq_linear takes for (M, bits, flags), a bq_route value, and the
+ * number of kernel passes in *passes (may be NULL); BQ_ERR_M or BQ_ERR_BITS
+ * for invalid arguments.  Host-only: launches nothing. */
+int bq_linear_route(int M, int bits, int flags, int* passes);
+
+/* sym detection -- section 二 path 2 (the symmetric variant applies when
+ * bias = -scale * ratio holds): writes 1 to the device int *flag when every
+ * stored fp16 bias equals -scale * ratio exactly (ratio (2^bits-1)/2, t5: 1),
+ * else 0, asynchronously on stream.  scales and biases: fp16 [N][K/gs],
+ * 2-byte aligned; flag: a caller-owned device int, 4-byte aligned.  A NaN
+ * anywhere gives 0.  When it is 1, bq_qmv_sym (bq_linear with
+ * BQ_LINEAR_SYM) gives the same bits as the affine call and skips the
+ * bias read. */
+int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits, int group_size, int* flag,
+                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,12 +37,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 1
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 2
 
 
 def test_strerror_covers_every_status(lib):
-    msgs = {s: bq.strerror(s) for s in range(-7, 1)}
-    assert len(set(msgs.values())) == 8
+    msgs = {s: bq.strerror(s) for s in range(-8, 1)}
+    assert len(set(msgs.values())) == 9
     assert bq.strerror(-99) == "unknown bq status"
 
 
@@ -176,3 +176,69 @@ def test_binding_tensor_helpers_refuse_cpu_tensors():
     s = torch.zeros(1, 1, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         bq.qmv_wide(x, w, s, s, 2, 64)
+
+
+# ---------------------------------------------------------------- dispatcher
+def test_linear_routes():
+    # bits 1/2: passes of up to five rows through the wide or symmetric kernel
+    for bits in (1, 2):
+        for M in (1, 2, 5):
+            assert bq.bq_linear_route(M, bits) == ("qmv_wide", 1)
+            assert bq.bq_linear_route(M, bits, bq.LINEAR_SYM) == ("qmv_sym", 1)
+        assert bq.bq_linear_route(6, bits) == ("qmv_wide", 2)
+        assert bq.bq_linear_route(16, bits) == ("qmv_wide", 4)
+        assert bq.bq_linear_route(17, bits, bq.LINEAR_SYM) == ("qmv_sym", 4)
+        assert bq.bq_linear_route(2048, bits) == ("qmv_wide", 410)
+    # t5: wide passes below 17 rows, the fused product from 17 (M > 16)
+    assert bq.T5_QMM_MIN_M == 17
+    for M in (1, 5):
+        assert bq.bq_linear_route(M, bq.BITS_T5) == ("t5_qmv_wide", 1)
+        assert bq.bq_linear_route(M, bq.BITS_T5, bq.LINEAR_SYM) == ("t5_qmv_wide", 1)
+    assert bq.bq_linear_route(16, bq.BITS_T5) == ("t5_qmv_wide", 4)
+    assert bq.bq_linear_route(17, bq.BITS_T5) == ("t5_qmm", 1)
+    assert bq.bq_linear_route(512, bq.BITS_T5) == ("t5_qmm", 1)
+
+
+def test_linear_route_errors(lib):
+    assert lib.bq_linear_route(0, 2, 0, None) == MRANGE
+    assert lib.bq_linear_route(-4, 2, 0, None) == MRANGE
+    assert lib.bq_linear_route(1, 3, 0, None) == BITS
+    with pytest.raises(bq.BQError):
+        bq.bq_linear_route(0, 2)
+
+
+FLAGS = -8
+
+
+def lcall(lib, x=PX, w=PW, s=PS, b=PB, y=PY, M=1, N=8, K=256, bits=2, gs=64, flags=0):
+    return lib.bq_linear(x, w, s, b, y, M, N, K, bits, gs, flags, None)
+
+
+def test_linear_validates_before_launch(lib):
+    assert lcall(lib, flags=2) == FLAGS
+    assert lcall(lib, flags=-1) == FLAGS
+    assert lcall(lib, M=0) == MRANGE
+    assert lcall(lib, bits=3) == BITS
+    assert lcall(lib, gs=32) == GROUP
+    assert lcall(lib, N=0) == SHAPE
+    assert lcall(lib, x=None) == NULL
+    assert lcall(lib, b=None) == NULL            # stored bias required without the sym flag
+    assert lcall(lib, x=PX + 8) == ALIGN
+    assert lcall(lib, s=PS + 8) == ALIGN
+    # t5 routes: wide below 17 rows, qmm from 17; both validate first
+    assert lcall(lib, bits=0, K=192, b=None) == ALIGN
+    assert lcall(lib, bits=0, M=17, K=192, b=None) == ALIGN
+    assert lcall(lib, bits=0, M=17, w=None, b=None) == NULL
+
+
+def test_sym_check_validates(lib):
+    vp = PX + 64
+    assert lib.bq_sym_check(None, PB, 8, 256, 2, 64, vp, None) == NULL
+    assert lib.bq_sym_check(PS, None, 8, 256, 2, 64, vp, None) == NULL
+    assert lib.bq_sym_check(PS, PB, 8, 256, 2, 64, None, None) == NULL
+    assert lib.bq_sym_check(PS, PB, 8, 256, 3, 64, vp, None) == BITS
+    assert lib.bq_sym_check(PS, PB, 8, 256, 2, 96, vp, None) == GROUP
+    assert lib.bq_sym_check(PS, PB, 0, 256, 2, 64, vp, None) == SHAPE
+    assert lib.bq_sym_check(PS, PB, 8, 200, 2, 64, vp, None) == SHAPE
+    assert lib.bq_sym_check(PS + 1, PB, 8, 256, 2, 64, vp, None) == ALIGN
+    assert lib.bq_sym_check(PS, PB, 8, 256, 2, 64, vp + 2, None) == ALIGN
