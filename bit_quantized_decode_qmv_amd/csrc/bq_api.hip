@@ -140,14 +140,12 @@ int launch_qmv_p(const QmvParams& p, void* stream) {
 // and every fetch past a slot's last unit still costs issue slots.
 template <int FMT, int GS, int M, bool IMPLIED>
 int launch_qmv_t(QmvParams p, void* stream) {
-  if constexpr (M <= 2) {
-    if (qmv_geometry(p, M, 4)) {
-      if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
-      return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);
-    }
+  if (qmv_geometry(p, M, 4)) {
+    if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
+    return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);
   }
   if (!qmv_geometry(p, M, 2)) return BQ_ERR_SHAPE;
-  return launch_qmv_p<FMT, GS, M, IMPLIED, 4, 2>(p, stream);
+  return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 2>(p, stream);
 }
 
 typedef int (*QmvLauncher)(QmvParams, void*);
