@@ -53,6 +53,8 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
       (uint64_t)N * (uint64_t)(K / gs) >= (1ull << 29))
     return BQ_ERR_SHAPE;
   if (e != E_DEQUANT && e != E_QMM && K / gs > kMaxDecodeGroups) return BQ_ERR_SHAPE;
+  // qmm addresses x with 32-bit offsets too
+  if (e == E_QMM && M > 0 && (uint64_t)M * (uint64_t)K * 2 >= (1ull << 31)) return BQ_ERR_SHAPE;
   if (e != E_DEQUANT) {
     if (M < 1) return BQ_ERR_M;
     if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
@@ -209,6 +211,48 @@ int run_qmv(Entry e, const void* x, const void* w, const void* scales, const voi
   return BQ_OK;
 }
 
+// ---------------------------------------------------------------- t5 qmm
+template <int BM, int GS, bool IMPLIED>
+int launch_qmm_t(const QmmParams& p, void* stream) {
+  const void* fn = reinterpret_cast<const void*>(&t5_qmm_kernel<BM, GS, IMPLIED>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmm_lds_bytes(256));
+  (void)attr;
+  dim3 grid((p.N + kQmmBN - 1) / kQmmBN, (p.M + BM - 1) / BM);
+  QmmParams q = p;
+  return launch(fn, grid, dim3(kQmmThreads), qmm_lds_bytes(BM), stream, &q);
+}
+
+template <int GS, bool IMPLIED>
+int launch_qmm_m(const QmmParams& p, void* stream) {
+  // rows of x per tile: enough to fill the tile, at most 256
+  if (p.M <= 32) return launch_qmm_t<32, GS, IMPLIED>(p, stream);
+  if (p.M <= 64) return launch_qmm_t<64, GS, IMPLIED>(p, stream);
+  if (p.M <= 128) return launch_qmm_t<128, GS, IMPLIED>(p, stream);
+  return launch_qmm_t<256, GS, IMPLIED>(p, stream);
+}
+
+int launch_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
+               int K, int group_size, void* stream) {
+  QmmParams p{};
+  p.x = static_cast<const half_t*>(x);
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = static_cast<const half_t*>(scales);
+  p.b = static_cast<const half_t*>(biases);
+  p.y = static_cast<half_t*>(y);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.G = K / group_size;
+  p.row_bytes = row_bytes_of(BQ_BITS_T5, K, group_size);
+  p.x_bytes = (int)((size_t)M * K * 2);
+  p.w_bytes = (int)((size_t)N * p.row_bytes);
+  p.sb_bytes = (int)((size_t)N * p.G * 2);
+  const bool implied = biases == nullptr;
+  if (group_size == 64) return implied ? launch_qmm_m<64, true>(p, stream) : launch_qmm_m<64, false>(p, stream);
+  return implied ? launch_qmm_m<128, true>(p, stream) : launch_qmm_m<128, false>(p, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,22 +306,7 @@ int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* bias
               int N, int K, int bits, int group_size, void* stream) {
   int st = validate(E_QMM, x, w, scales, biases, y, M, N, K, bits, group_size);
   if (st != BQ_OK) return st;
-  QmmParams p{};
-  p.x = static_cast<const half_t*>(x);
-  p.w = static_cast<const uint8_t*>(w);
-  p.s = static_cast<const half_t*>(scales);
-  p.b = static_cast<const half_t*>(biases);
-  p.y = static_cast<half_t*>(y);
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.G = K / group_size;
-  p.gs = group_size;
-  p.row_bytes = row_bytes_of(BQ_BITS_T5, K, group_size);
-  dim3 grid((N + kQmmBN - 1) / kQmmBN, (M + kQmmBM - 1) / kQmmBM);
-  const void* fn = biases ? reinterpret_cast<const void*>(&t5_qmm_kernel<false>)
-                          : reinterpret_cast<const void*>(&t5_qmm_kernel<true>);
-  return launch(fn, grid, dim3(256), 0, stream, &p);
+  return launch_qmm(x, w, scales, biases, y, M, N, K, group_size, stream);
 }
 
 int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,

@@ -3,16 +3,28 @@
 //
 // Method: "oMLX Bonsai 自定义内核" article, section 二 path 3 -- for prefill
 // with more than 16 rows the t5 weights go through a fused "unpack + matrix
-// multiply" kernel that reads each t5 byte once.
+// multiply" kernel that reads each t5 byte once per weight tile.
 //
-// gfx950 design: a 256-thread workgroup computes a 128x128 tile of y; the
-// K loop steps 128 codes at a time.  Per step the x tile (128x128 fp16) is
-// copied to LDS and the 128 rows x 26 bytes of t5 weights are read once
-// from HBM, decoded through a base-3 digit table and written to LDS as fp16
-// weights w = s*(q-1) (exact in fp16 when the bias is -scale) or the
-// correctly rounded fp16 of s*q+b.  Each wave then runs 4x4
-// v_mfma_f32_16x16x32_f16 tiles (64x64 of y) over the step with fp32
-// accumulators.
+// gfx950 design
+// -------------
+// * A 256-thread workgroup (4 waves) computes a BM x 128 tile of y; the K
+//   loop steps 64 codes at a time.  Each wave owns a (BM/2) x 64 block and
+//   runs v_mfma_f32_16x16x32_f16 on it with fp32 accumulators.
+// * x tiles go straight from HBM/L2 to LDS with buffer loads that write LDS
+//   (no registers, no ALU), into a double buffer.  Rows are 128 bytes of
+//   eight 16-byte units, stored at unit (q XOR row%8) so that the MFMA
+//   operand reads of 16 rows hit distinct banks.
+// * Weights: each thread decodes 32 codes of one weight row per step.  The
+//   step's t5 bytes (at most 8 per thread) are loaded one step ahead as three
+//   dwords and realigned; a 256-entry LDS table gives each byte's five digits
+//   as 6-bit fields holding 16*digit, which is the shift that picks the
+//   code's fp16 weight out of the row's three possible weights held in one
+//   64-bit register: {-s, 0, s} when the bias is -scale (exact), otherwise
+//   the correctly rounded s*q + b for q = 0, 1, 2.  Two codes then cost one
+//   bit-field extract and one 64-bit shift each plus one pack.
+// * Software pipeline per step: issue the x loads of the next step, multiply
+//   the current step, decode the next step's weights into the other buffer,
+//   issue the byte and scale loads of the step after, then one barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,6 +37,7 @@ namespace bq {
 
 typedef half_t half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 struct QmmParams {
   const half_t* x;     // [M][K]
@@ -32,118 +45,225 @@ struct QmmParams {
   const half_t* s;     // [N][G]
   const half_t* b;     // [N][G] or null (implied -scale)
   half_t* y;           // [M][N]
-  int M, N, K, G, gs, row_bytes;
+  int M, N, K, G, row_bytes;
+  int x_bytes, w_bytes, sb_bytes;  // buffer descriptor sizes
 };
 
-constexpr int kQmmBM = 128, kQmmBN = 128, kQmmBK = 128;
-constexpr int kQmmLd = kQmmBK + 8;  // LDS row stride in halves (272 B)
+constexpr int kQmmBN = 128;       // weight rows per tile
+constexpr int kQmmBK = 64;        // codes per K step
+constexpr int kQmmThreads = 256;  // 4 waves
 
-template <bool IMPLIED>
-__global__ __launch_bounds__(256) void t5_qmm_kernel(QmmParams p) {
-  __shared__ __attribute__((aligned(16))) half_t xs[kQmmBM * kQmmLd];
-  __shared__ __attribute__((aligned(16))) half_t ws[kQmmBN * kQmmLd];
-  __shared__ uint32_t raw[kQmmBN * 8];   // 7 dwords of t5 bytes per row (+1 pad)
-  __shared__ uint16_t lut[256];
+constexpr size_t qmm_lds_bytes(int BM) {
+  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * kQmmBN * kQmmBK * 2 + 256 * 4;
+}
+
+// 16-byte unit (row, q) of a 128-byte LDS row
+__device__ __forceinline__ int qmm_swz(int row, int q) { return row * 8 + (q ^ (row & 7)); }
+
+// Digit table entry: digit i of byte v, times 16, in bits 6i..6i+5.
+__device__ __forceinline__ uint32_t t5_shift_fields(uint32_t v) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    f |= ((v % 3u) * 16u) << (6 * i);
+    v /= 3u;
+  }
+  return f;
+}
+
+// Where code c (0..GS-1) of a group sits in the group's bytes: 64-groups
+// hold code 5j+i at digit i of byte j; 128-groups are two 13-byte halves,
+// codes 0..64 in bytes 0..12 and codes 65..127 in bytes 13..25.
+template <int GS> constexpr int t5_byte_of(int c) { return (GS == 128 && c >= 65) ? 13 + (c - 65) / 5 : c / 5; }
+template <int GS> constexpr int t5_digit_of(int c) { return (GS == 128 && c >= 65) ? (c - 65) % 5 : c % 5; }
+
+// A thread's 32 codes in a step: codes 64*PAR + 32*H + u of the group
+// (PAR: which half of a 128-group the step covers; always 0 for 64-groups).
+template <int GS, int PAR, int H> struct T5Span {
+  static constexpr int c0 = 64 * PAR + 32 * H;
+  static constexpr int start = t5_byte_of<GS>(c0);  // first byte, within the group
+};
+
+// Decodes the thread's 32 codes: bytes = the 8 bytes from the span's first
+// byte (two dwords), wt = the row's three fp16 weights (bits 0-15: q = 0,
+// 16-31: q = 1, 32-47: q = 2), lut = digit table.  Out: 16 dwords, code
+// pairs (2t, 2t+1) in dword t.
+template <int GS, int PAR, int H>
+__device__ __forceinline__ void t5_decode32(uint32_t w0, uint32_t w1, uint64_t wt, const uint32_t* lut,
+                                            uint32_t (&out)[16]) {
+  using S = T5Span<GS, PAR, H>;
+  constexpr int nb = t5_byte_of<GS>(S::c0 + 31) - S::start + 1;  // bytes used, <= 8
+  uint32_t f[8];
+#pragma unroll
+  for (int j = 0; j < nb; ++j) f[j] = lut[((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = S::c0 + 2 * t + e;
+      const int j = t5_byte_of<GS>(c) - S::start;
+      const int d = t5_digit_of<GS>(c);
+      const uint32_t shift = (f[j] >> (6 * d)) & 63u;
+      h[e] = (uint32_t)(wt >> shift) & 0xFFFFu;
+    }
+    out[t] = h[0] | (h[1] << 16);
+  }
+}
+
+template <int BM, int GS, bool IMPLIED>
+__global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
+  constexpr int MB = BM / 32;  // 16-row MFMA blocks per wave (wave rows: BM/2)
+  extern __shared__ __attribute__((aligned(16))) uint32_t qsmem[];
+  half_t* xs = reinterpret_cast<half_t*>(qsmem);                  // [2][BM*64]
+  half_t* ws = xs + 2 * BM * kQmmBK;                              // [2][128*64]
+  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * kQmmBN * kQmmBK);  // [256]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kQmmBM;
+  const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * kQmmBN;
+  const int S = p.K / kQmmBK;
 
-  lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.sb_bytes);
+  const rsrc_t rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
 
-  float4_t acc[4][4];
+  lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
+
+  // ---- x loads: chunk c = i*4 + wave covers LDS units [64c, 64c+64) of a
+  // buffer, rows 8c..8c+7; lane l loads unit 64c+l
+  auto issue_x = [&](int step, int buf) {
+    const int k0 = step * kQmmBK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BM / 32; ++i) {
+      const int c = i * 4 + wave;
+      const int u = c * 64 + lane;
+      const int row = u >> 3, q = (u & 7) ^ (row & 7);
+      const uint32_t off = 2u * ((uint32_t)(m0 + row) * (uint32_t)p.K + (uint32_t)(k0 + q * 8));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(xs + buf * BM * kQmmBK + c * 512), 16, (int)off, 0, 0, 0);
+    }
+  };
+
+  // ---- weight rows: thread -> row r, codes 32h..32h+31 of each step
+  const int r = tid & 127, h = tid >> 7;
+  const uint32_t row_off = (uint32_t)(n0 + r) * (uint32_t)p.row_bytes;
+  const uint32_t sb_row = (uint32_t)(n0 + r) * (uint32_t)p.G;
+  struct Raw {
+    u32x3 d;
+    uint16_t s, b;
+  };
+  auto group_base = [&](int step) { return GS == 64 ? 13 * step : 26 * (step >> 1); };
+  auto span_start = [&](int step) {
+    const int par = GS == 128 ? (step & 1) : 0;
+    return par == 0 ? (h == 0 ? T5Span<GS, 0, 0>::start : T5Span<GS, 0, 1>::start)
+                    : (h == 0 ? T5Span<GS, 1, 0>::start : T5Span<GS, 1, 1>::start);
+  };
+  auto issue_raw = [&](int step, Raw& rw_) {
+    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
+    rw_.d = __builtin_amdgcn_raw_buffer_load_b96(rw, (int)(a & ~3u), 0, 0);
+    const uint32_t so = 2u * (sb_row + (uint32_t)((step * kQmmBK) / GS));
+    rw_.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+    if constexpr (!IMPLIED) rw_.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, 0, 0);
+    else rw_.b = 0;
+  };
+  auto decode = [&](int step, const Raw& rw_, int buf) {
+    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
+    const uint32_t sh = a & 3u;
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(rw_.d[1], rw_.d[0], sh);
+    const uint32_t w1 = __builtin_amdgcn_alignbyte(rw_.d[2], rw_.d[1], sh);
+    uint64_t wt;
+    if constexpr (IMPLIED) {
+      const uint32_t sp = rw_.s, sn = rw_.s ^ 0x8000u;  // +s, -s (exact)
+      wt = (uint64_t)sn | ((uint64_t)sp << 32);
+    } else {
+      const float s = h2f(__builtin_bit_cast(half_t, rw_.s)), b = h2f(__builtin_bit_cast(half_t, rw_.b));
+      const uint32_t v0 = __builtin_bit_cast(uint16_t, affine_to_half(s, 0u, b));
+      const uint32_t v1 = __builtin_bit_cast(uint16_t, affine_to_half(s, 1u, b));
+      const uint32_t v2 = __builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b));
+      wt = (uint64_t)(v0 | (v1 << 16)) | ((uint64_t)v2 << 32);
+    }
+    uint32_t out[16];
+    const int par = GS == 128 ? (step & 1) : 0;
+    if (par == 0) {
+      if (h == 0) t5_decode32<GS, 0, 0>(w0, w1, wt, lut, out);
+      else t5_decode32<GS, 0, 1>(w0, w1, wt, lut, out);
+    } else {
+      if (h == 0) t5_decode32<GS, (GS == 128 ? 1 : 0), 0>(w0, w1, wt, lut, out);
+      else t5_decode32<GS, (GS == 128 ? 1 : 0), 1>(w0, w1, wt, lut, out);
+    }
+    half_t* wb = ws + buf * kQmmBN * kQmmBK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<u32x4*>(wb + qmm_swz(r, 4 * h + t) * 8) =
+          u32x4{out[4 * t], out[4 * t + 1], out[4 * t + 2], out[4 * t + 3]};
+  };
+
+  float4_t acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = p.K / kQmmBK;
-  const int gb = (p.gs + 4) / 5;             // 13 or 26 bytes per group
-  for (int st = 0; st < nsteps; ++st) {
-    const int k0 = st * kQmmBK;
-    __syncthreads();
-    // x tile: 128 rows x 256 B; thread -> (row, 16-byte piece), 8 passes
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 256 + tid;
-      const int r = idx >> 4, c = (idx & 15) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m0 + r < p.M) v = *reinterpret_cast<const u32x4*>(p.x + (size_t)(m0 + r) * p.K + k0 + c);
-      *reinterpret_cast<u32x4*>(&xs[r * kQmmLd + c]) = v;
-    }
-    // raw t5 bytes of the step: 26 bytes per row from byte 26*st, read as the
-    // 7 dwords that cover them (rows are whole dwords, offset 0 or 2)
-    for (int idx = tid; idx < kQmmBN * 7; idx += 256) {
-      const int r = idx / 7, d = idx % 7;
-      uint32_t v = 0u;
-      if (n0 + r < p.N) {
-        const uint8_t* rp = p.w + (size_t)(n0 + r) * p.row_bytes + ((26 * st) & ~3);
-        v = reinterpret_cast<const uint32_t*>(rp)[d];
-      }
-      raw[r * 8 + d] = v;
-    }
-    __syncthreads();
-    // decode: thread -> (row, 8-code segment), 8 segments per thread
-    const int sh = (26 * st) & 3;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 256 + tid;
-      const int r = idx >> 4, seg = idx & 15;
-      const int kk0 = seg * 8;
-      uint32_t out[4] = {0u, 0u, 0u, 0u};
-      if (n0 + r < p.N) {
-        const uint8_t* rb = reinterpret_cast<const uint8_t*>(raw + r * 8) + sh;
-        const int grp0 = (k0 + kk0) / p.gs;  // a segment never spans two groups
-        const float s = (float)p.s[(size_t)(n0 + r) * p.G + grp0];
-        const float b = IMPLIED ? -s : (float)p.b[(size_t)(n0 + r) * p.G + grp0];
-        const int gbase = (p.gs == 64) ? (kk0 >= 64 ? 13 : 0) : 0;
-        const int kg0 = (p.gs == 64) ? (kk0 & 63) : kk0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int kg = kg0 + u;
-          const uint32_t fields = lut[rb[gbase + kg / 5]];
-          const uint32_t q = (fields >> (2 * (kg % 5))) & 3u;
-          half_t wv;
-          if (IMPLIED) wv = (half_t)(s * (float)((int)q - 1));
-          else wv = affine_to_half(s, q, b);
-          const uint32_t hb = __builtin_bit_cast(uint16_t, wv);
-          out[u >> 1] |= hb << (16 * (u & 1));
-        }
-      }
-      *reinterpret_cast<u32x4*>(&ws[r * kQmmLd + kk0]) = u32x4{out[0], out[1], out[2], out[3]};
-    }
-    (void)gb;
-    __syncthreads();
-    // MFMA over the step: 4 sub-steps of 32 codes
+  auto multiply = [&](int buf) {
+    const half_t* xb = xs + buf * BM * kQmmBK;
+    const half_t* wb = ws + buf * kQmmBN * kQmmBK;
 #pragma unroll
     for (int ks = 0; ks < kQmmBK / 32; ++ks) {
-      half8_t af[4], bf[4];
-      const int kc = ks * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&xs[(wm * 64 + 16 * i + (lane & 15)) * kQmmLd + kc]);
+      const int q = ks * 4 + (lane >> 4);
+      half8_t bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(&ws[(wn * 64 + 16 * j + (lane & 15)) * kQmmLd + kc]);
+        bf[j] = *reinterpret_cast<const half8_t*>(wb + qmm_swz(wn * 64 + 16 * j + (lane & 15), q) * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MB; ++i) {
+        const half8_t af =
+            *reinterpret_cast<const half8_t*>(xb + qmm_swz(wm * (BM / 2) + 16 * i + (lane & 15), q) * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
     }
+  };
+
+  // ---- prologue: step 0 in buffer 0, raw bytes of step 1 in registers
+  Raw raw;
+  issue_x(0, 0);
+  issue_raw(0, raw);
+  __syncthreads();  // table built (the loads above are waited for by decode)
+  decode(0, raw, 0);
+  if (S > 1) issue_raw(1, raw);
+  __syncthreads();  // x of step 0 (this wave's loads completed by the fence) and weights of step 0
+
+  // loads issued after a step's x loads: bytes + scale (+ bias)
+  constexpr int kRawLoads = IMPLIED ? 2 : 3;
+  for (int st = 0; st < S; ++st) {
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st + 1 < S) issue_x(st + 1, nxt);
+    multiply(cur);
+    if (st + 1 < S) decode(st + 1, raw, nxt);
+    // always issued (the last steps reload the last step's bytes, unused),
+    // so that the count of loads after the x loads is fixed
+    issue_raw(min(st + 2, S - 1), raw);
+    // this wave's x loads of step st+1 have landed in LDS (only the loads
+    // issued after them may still be in flight), its weight stores are done;
+    // then every wave is past step st
+    __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
 
   // D layout of 16x16x32: lane holds rows 4*(lane/16)+v, column lane%16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + v;
+        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + v;
         const int n = n0 + wn * 64 + 16 * j + (lane & 15);
         if (m < p.M && n < p.N) p.y[(size_t)m * p.N + n] = (half_t)acc[i][j][v];
       }
