@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "bq.h"
 #include "dequant_kernels.hpp"
@@ -212,24 +213,65 @@ int run_qmv(Entry e, const void* x, const void* w, const void* scales, const voi
 }
 
 // ---------------------------------------------------------------- t5 qmm
-template <int BM, int GS, bool IMPLIED>
+template <int BM, int BN, int GS, bool IMPLIED>
 int launch_qmm_t(const QmmParams& p, void* stream) {
-  const void* fn = reinterpret_cast<const void*>(&t5_qmm_kernel<BM, GS, IMPLIED>);
+  const void* fn = reinterpret_cast<const void*>(&t5_qmm_kernel<BM, BN, GS, IMPLIED>);
   static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmm_lds_bytes(256));
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmm_lds_bytes(BM, BN));
   (void)attr;
-  dim3 grid((p.N + kQmmBN - 1) / kQmmBN, (p.M + BM - 1) / BM);
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   QmmParams q = p;
-  return launch(fn, grid, dim3(kQmmThreads), qmm_lds_bytes(BM), stream, &q);
+  return launch(fn, grid, dim3(kQmmThreads), qmm_lds_bytes(BM, BN), stream, &q);
+}
+
+// Estimated cycles of one call with BM x BN tiles: per K step the larger of
+// the MFMA cycles and the LDS cycles (operand reads, tile writes), plus the
+// weight-decoding ALU cycles (measured not to overlap the MFMAs), times the
+// rounds of workgroups over 256 CUs; against the L2 / last-level-cache
+// traffic of re-reading x once per column of tiles and W once per row of
+// tiles at 32 bytes per clock per CU.  Only the order of the estimates
+// matters: it picks the tile shape.
+double qmm_cost(int M, int N, int K, int BM, int BN) {
+  const double mfma = (double)BM * BN / 32.0;
+  const double lds = 64.0 * (BM / 32 + BN / 32) + (BM + BN);
+  const double alu = 2.5 * BN;
+  const double step = std::max(mfma, lds) + alu;
+  const double tiles = (double)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  const int per_cu = qmm_lds_bytes(BM, BN) * 2 <= 160 * 1024 ? 2 : 1;
+  const double rounds = std::ceil(tiles / (256.0 * per_cu));
+  const double compute = rounds * per_cu * (K / kQmmBK) * step;
+  const double traffic = ((double)M * K * 2 * ((N + BN - 1) / BN) + (double)N * K * 0.2 * ((M + BM - 1) / BM)) /
+                         (256.0 * 32.0);
+  return std::max(compute, traffic);
 }
 
 template <int GS, bool IMPLIED>
 int launch_qmm_m(const QmmParams& p, void* stream) {
-  // rows of x per tile: enough to fill the tile, at most 256
-  if (p.M <= 32) return launch_qmm_t<32, GS, IMPLIED>(p, stream);
-  if (p.M <= 64) return launch_qmm_t<64, GS, IMPLIED>(p, stream);
-  if (p.M <= 128) return launch_qmm_t<128, GS, IMPLIED>(p, stream);
-  return launch_qmm_t<256, GS, IMPLIED>(p, stream);
+  typedef int (*Fn)(const QmmParams&, void*);
+  struct Cand {
+    int bm, bn;
+    Fn fn;
+  };
+  // the shapes the estimate picks over M 1..4096, N 256..65536, K 256..17408
+  // (128 x 256 tiles, which it picks for a few, do not fit the registers of
+  // the two wave kinds)
+  static const Cand cands[] = {
+      {32, 64, &launch_qmm_t<32, 64, GS, IMPLIED>},     {32, 128, &launch_qmm_t<32, 128, GS, IMPLIED>},
+      {64, 64, &launch_qmm_t<64, 64, GS, IMPLIED>},     {64, 256, &launch_qmm_t<64, 256, GS, IMPLIED>},
+      {128, 64, &launch_qmm_t<128, 64, GS, IMPLIED>},   {256, 64, &launch_qmm_t<256, 64, GS, IMPLIED>},
+      {256, 128, &launch_qmm_t<256, 128, GS, IMPLIED>},
+  };
+  const Cand* best = nullptr;
+  double best_cost = 0.0;
+  for (const Cand& c : cands) {
+    if (c.bm > 32 && c.bm / 2 >= p.M) continue;  // a tile at least half full of rows
+    const double cost = qmm_cost(p.M, p.N, p.K, c.bm, c.bn);
+    if (!best || cost < best_cost) {
+      best = &c;
+      best_cost = cost;
+    }
+  }
+  return best->fn(p, stream);
 }
 
 int launch_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,

@@ -7,24 +7,28 @@
 //
 // gfx950 design
 // -------------
-// * A 256-thread workgroup (4 waves) computes a BM x 128 tile of y; the K
-//   loop steps 64 codes at a time.  Each wave owns a (BM/2) x 64 block and
-//   runs v_mfma_f32_16x16x32_f16 on it with fp32 accumulators.
+// * A 512-thread workgroup computes a BM x BN tile of y (BM 32 to 256, BN
+//   64 to 256, chosen per call from an estimate of its cost); the K loop
+//   steps 64 codes at a time.  Four waves multiply: each owns a
+//   (BM/2) x (BN/2) block and runs v_mfma_f32_16x16x32_f16 on it with fp32
+//   accumulators.  Four more waves load the next step's x and decode its
+//   weights meanwhile; each SIMD holds one wave of each kind, so the matrix
+//   cores and the vector ALUs run at the same time.
 // * x tiles go straight from HBM/L2 to LDS with buffer loads that write LDS
 //   (no registers, no ALU), into a double buffer.  Rows are 128 bytes of
 //   eight 16-byte units, stored at unit (q XOR row%8) so that the MFMA
 //   operand reads of 16 rows hit distinct banks.
-// * Weights: each thread decodes 32 codes of one weight row per step.  The
-//   step's t5 bytes (at most 8 per thread) are loaded one step ahead as three
-//   dwords and realigned; a 256-entry LDS table gives each byte's five digits
+// * Weights: each decoding thread takes BN/4 codes of one weight row per
+//   step.  Their t5 bytes (at most 14) are loaded one step ahead as a
+//   16-byte window and realigned; a 256-entry LDS table gives each byte's five digits
 //   as 6-bit fields holding 16*digit, which is the shift that picks the
 //   code's fp16 weight out of the row's three possible weights held in one
 //   64-bit register: {-s, 0, s} when the bias is -scale (exact), otherwise
 //   the correctly rounded s*q + b for q = 0, 1, 2.  Two codes then cost one
 //   bit-field extract and one 64-bit shift each plus one pack.
-// * Software pipeline per step: issue the x loads of the next step, multiply
-//   the current step, decode the next step's weights into the other buffer,
-//   issue the byte and scale loads of the step after, then one barrier.
+// * Per step: the multiplying waves work on one buffer while the others fill
+//   the second one (x loads, weight decode, and the byte and scale loads of
+//   the step after); then one barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,7 +41,6 @@ namespace bq {
 
 typedef half_t half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 struct QmmParams {
   const half_t* x;     // [M][K]
@@ -49,12 +52,11 @@ struct QmmParams {
   int x_bytes, w_bytes, sb_bytes;  // buffer descriptor sizes
 };
 
-constexpr int kQmmBN = 128;       // weight rows per tile
 constexpr int kQmmBK = 64;        // codes per K step
-constexpr int kQmmThreads = 256;  // 4 waves
+constexpr int kQmmThreads = 512;  // 4 MFMA waves (2 x 2 over the tile) + 4 loading/decoding waves
 
-constexpr size_t qmm_lds_bytes(int BM) {
-  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * kQmmBN * kQmmBK * 2 + 256 * 4;
+constexpr size_t qmm_lds_bytes(int BM, int BN) {
+  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * BN * kQmmBK * 2 + 256 * 4;
 }
 
 // 16-byte unit (row, q) of a 128-byte LDS row
@@ -77,27 +79,28 @@ __device__ __forceinline__ uint32_t t5_shift_fields(uint32_t v) {
 template <int GS> constexpr int t5_byte_of(int c) { return (GS == 128 && c >= 65) ? 13 + (c - 65) / 5 : c / 5; }
 template <int GS> constexpr int t5_digit_of(int c) { return (GS == 128 && c >= 65) ? (c - 65) % 5 : c % 5; }
 
-// A thread's 32 codes in a step: codes 64*PAR + 32*H + u of the group
+// A thread's NC codes in a step: codes 64*PAR + NC*H + u of the group
 // (PAR: which half of a 128-group the step covers; always 0 for 64-groups).
-template <int GS, int PAR, int H> struct T5Span {
-  static constexpr int c0 = 64 * PAR + 32 * H;
+template <int GS, int PAR, int H, int NC> struct T5Span {
+  static constexpr int c0 = 64 * PAR + NC * H;
   static constexpr int start = t5_byte_of<GS>(c0);  // first byte, within the group
 };
 
-// Decodes the thread's 32 codes: bytes = the 8 bytes from the span's first
-// byte (two dwords), wt = the row's three fp16 weights (bits 0-15: q = 0,
-// 16-31: q = 1, 32-47: q = 2), lut = digit table.  Out: 16 dwords, code
-// pairs (2t, 2t+1) in dword t.
-template <int GS, int PAR, int H>
-__device__ __forceinline__ void t5_decode32(uint32_t w0, uint32_t w1, uint64_t wt, const uint32_t* lut,
-                                            uint32_t (&out)[16]) {
-  using S = T5Span<GS, PAR, H>;
-  constexpr int nb = t5_byte_of<GS>(S::c0 + 31) - S::start + 1;  // bytes used, <= 8
-  uint32_t f[8];
+// Decodes the thread's NC codes: wv = the 16 bytes from the span's first
+// byte, wt = the row's three fp16 weights (bits 0-15: q = 0, 16-31: q = 1,
+// 32-47: q = 2), lut = digit table.  Out: NC/2 dwords, code pairs (2t, 2t+1)
+// in dword t.
+template <int GS, int PAR, int H, int NC>
+__device__ __forceinline__ void t5_decode(const uint32_t (&wv)[4], uint64_t wt, const uint32_t* lut,
+                                          uint32_t (&out)[NC / 2]) {
+  using S = T5Span<GS, PAR, H, NC>;
+  constexpr int nb = t5_byte_of<GS>(S::c0 + NC - 1) - S::start + 1;  // bytes used
+  static_assert(nb <= 14, "span of at most 14 bytes");
+  uint32_t f[14];
 #pragma unroll
-  for (int j = 0; j < nb; ++j) f[j] = lut[((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu];
+  for (int j = 0; j < nb; ++j) f[j] = lut[(wv[j >> 2] >> (8 * (j & 3))) & 0xFFu];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  for (int t = 0; t < NC / 2; ++t) {
     uint32_t h[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -111,20 +114,57 @@ __device__ __forceinline__ void t5_decode32(uint32_t w0, uint32_t w1, uint64_t w
   }
 }
 
-template <int BM, int GS, bool IMPLIED>
+// The span start and the decode for a runtime span index h < 64/NC (the
+// same for a whole wave), dispatched to the compile-time instances.
+template <int GS, int PAR, int NC>
+__device__ __forceinline__ int t5_span_start(int h) {
+  int st = T5Span<GS, PAR, 0, NC>::start;
+  if constexpr (64 / NC > 1) {
+    if (h == 1) st = T5Span<GS, PAR, 1, NC>::start;
+  }
+  if constexpr (64 / NC > 2) {
+    if (h == 2) st = T5Span<GS, PAR, 2, NC>::start;
+    if (h == 3) st = T5Span<GS, PAR, 3, NC>::start;
+  }
+  return st;
+}
+
+template <int GS, int PAR, int NC>
+__device__ __forceinline__ void t5_decode_h(int h, const uint32_t (&wv)[4], uint64_t wt, const uint32_t* lut,
+                                            uint32_t (&out)[NC / 2]) {
+  if (h == 0) t5_decode<GS, PAR, 0, NC>(wv, wt, lut, out);
+  if constexpr (64 / NC > 1) {
+    if (h == 1) t5_decode<GS, PAR, 1, NC>(wv, wt, lut, out);
+  }
+  if constexpr (64 / NC > 2) {
+    if (h == 2) t5_decode<GS, PAR, 2, NC>(wv, wt, lut, out);
+    if (h == 3) t5_decode<GS, PAR, 3, NC>(wv, wt, lut, out);
+  }
+}
+
+template <int BM, int BN, int GS, bool IMPLIED>
 __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
-  constexpr int MB = BM / 32;  // 16-row MFMA blocks per wave (wave rows: BM/2)
+  constexpr int MB = BM / 32;   // 16-row MFMA blocks per wave (wave rows: BM/2)
+  constexpr int NB = BN / 32;   // 16-column MFMA blocks per wave (wave columns: BN/2)
+  constexpr int NC = BN / 4;    // codes a thread decodes per step
+  constexpr int RPW = 64 / NC;  // spans per weight row (threads per row)
   extern __shared__ __attribute__((aligned(16))) uint32_t qsmem[];
   half_t* xs = reinterpret_cast<half_t*>(qsmem);                  // [2][BM*64]
-  half_t* ws = xs + 2 * BM * kQmmBK;                              // [2][128*64]
-  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * kQmmBN * kQmmBK);  // [256]
+  half_t* ws = xs + 2 * BM * kQmmBK;                              // [2][BN*64]
+  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * BN * kQmmBK);  // [256]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * kQmmBN;
+  // waves 0-3 multiply, waves 4-7 load x and decode weights; each SIMD runs
+  // one of each, so the matrix cores and the vector ALUs work side by side
+  const bool producer = wave >= 4;
+  const int pw = wave & 3;             // producer wave index
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int t = (int)blockIdx.x;
+  const int m0 = (t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
   const int S = p.K / kQmmBK;
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
@@ -132,15 +172,15 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
   const rsrc_t rs = make_rsrc(p.s, p.sb_bytes);
   const rsrc_t rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
 
-  lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
+  if (tid < 256) lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
 
-  // ---- x loads: chunk c = i*4 + wave covers LDS units [64c, 64c+64) of a
-  // buffer, rows 8c..8c+7; lane l loads unit 64c+l
+  // ---- x loads (producers): chunk c = i*4 + pw covers LDS units
+  // [64c, 64c+64) of a buffer, rows 8c..8c+7; lane l loads unit 64c+l
   auto issue_x = [&](int step, int buf) {
     const int k0 = step * kQmmBK;
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) {
-      const int c = i * 4 + wave;
+      const int c = i * 4 + pw;
       const int u = c * 64 + lane;
       const int row = u >> 3, q = (u & 7) ^ (row & 7);
       const uint32_t off = 2u * ((uint32_t)(m0 + row) * (uint32_t)p.K + (uint32_t)(k0 + q * 8));
@@ -149,23 +189,30 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
     }
   };
 
-  // ---- weight rows: thread -> row r, codes 32h..32h+31 of each step
-  const int r = tid & 127, h = tid >> 7;
+  // ---- weight rows (producers): thread -> row r, codes NC*h .. NC*h+NC-1
+  // of each step (h is the same for a whole wave)
+  const int pt = tid & 255;
+  const int r = pt % BN, h = pt / BN;
+  static_assert(RPW * BN == 256, "one span per producer thread");
   const uint32_t row_off = (uint32_t)(n0 + r) * (uint32_t)p.row_bytes;
   const uint32_t sb_row = (uint32_t)(n0 + r) * (uint32_t)p.G;
   struct Raw {
-    u32x3 d;
+    u32x4 d;
     uint16_t s, b;
   };
   auto group_base = [&](int step) { return GS == 64 ? 13 * step : 26 * (step >> 1); };
+  constexpr int P1 = GS == 128 ? 1 : 0;
   auto span_start = [&](int step) {
     const int par = GS == 128 ? (step & 1) : 0;
-    return par == 0 ? (h == 0 ? T5Span<GS, 0, 0>::start : T5Span<GS, 0, 1>::start)
-                    : (h == 0 ? T5Span<GS, 1, 0>::start : T5Span<GS, 1, 1>::start);
+    return par == 0 ? t5_span_start<GS, 0, NC>(h) : t5_span_start<GS, P1, NC>(h);
   };
   auto issue_raw = [&](int step, Raw& rw_) {
     const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
-    rw_.d = __builtin_amdgcn_raw_buffer_load_b96(rw, (int)(a & ~3u), 0, 0);
+    // 16 bytes from the dword at or below the span's first byte: a span has
+    // at most 13 bytes (14 for the second half of a 128-group, which starts
+    // 0 or 2 bytes into its dword), so the window always holds it; dwords
+    // past the end of W read as zeros
+    rw_.d = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(a & ~3u), 0, 0);
     const uint32_t so = 2u * (sb_row + (uint32_t)((step * kQmmBK) / GS));
     rw_.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
     if constexpr (!IMPLIED) rw_.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, 0, 0);
@@ -174,8 +221,9 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
   auto decode = [&](int step, const Raw& rw_, int buf) {
     const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
     const uint32_t sh = a & 3u;
-    const uint32_t w0 = __builtin_amdgcn_alignbyte(rw_.d[1], rw_.d[0], sh);
-    const uint32_t w1 = __builtin_amdgcn_alignbyte(rw_.d[2], rw_.d[1], sh);
+    uint32_t wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(k < 3 ? rw_.d[k + 1] : 0u, rw_.d[k], sh);
     uint64_t wt;
     if constexpr (IMPLIED) {
       const uint32_t sp = rw_.s, sn = rw_.s ^ 0x8000u;  // +s, -s (exact)
@@ -187,84 +235,90 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
       const uint32_t v2 = __builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b));
       wt = (uint64_t)(v0 | (v1 << 16)) | ((uint64_t)v2 << 32);
     }
-    uint32_t out[16];
+    uint32_t out[NC / 2];
     const int par = GS == 128 ? (step & 1) : 0;
-    if (par == 0) {
-      if (h == 0) t5_decode32<GS, 0, 0>(w0, w1, wt, lut, out);
-      else t5_decode32<GS, 0, 1>(w0, w1, wt, lut, out);
-    } else {
-      if (h == 0) t5_decode32<GS, (GS == 128 ? 1 : 0), 0>(w0, w1, wt, lut, out);
-      else t5_decode32<GS, (GS == 128 ? 1 : 0), 1>(w0, w1, wt, lut, out);
-    }
-    half_t* wb = ws + buf * kQmmBN * kQmmBK;
+    if (par == 0) t5_decode_h<GS, 0, NC>(h, wv, wt, lut, out);
+    else t5_decode_h<GS, P1, NC>(h, wv, wt, lut, out);
+    half_t* wb = ws + buf * BN * kQmmBK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      *reinterpret_cast<u32x4*>(wb + qmm_swz(r, 4 * h + t) * 8) =
+    for (int t = 0; t < NC / 8; ++t)
+      *reinterpret_cast<u32x4*>(wb + qmm_swz(r, (NC / 8) * h + t) * 8) =
           u32x4{out[4 * t], out[4 * t + 1], out[4 * t + 2], out[4 * t + 3]};
   };
 
-  float4_t acc[MB][4];
+  float4_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   auto multiply = [&](int buf) {
     const half_t* xb = xs + buf * BM * kQmmBK;
-    const half_t* wb = ws + buf * kQmmBN * kQmmBK;
+    const half_t* wb = ws + buf * BN * kQmmBK;
 #pragma unroll
     for (int ks = 0; ks < kQmmBK / 32; ++ks) {
       const int q = ks * 4 + (lane >> 4);
-      half8_t bf[4];
+      half8_t bf[NB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(wb + qmm_swz(wn * 64 + 16 * j + (lane & 15), q) * 8);
+      for (int j = 0; j < NB; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(wb + qmm_swz(wn * (BN / 2) + 16 * j + (lane & 15), q) * 8);
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const half8_t af =
             *reinterpret_cast<const half8_t*>(xb + qmm_swz(wm * (BM / 2) + 16 * i + (lane & 15), q) * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
       }
     }
   };
 
   // ---- prologue: step 0 in buffer 0, raw bytes of step 1 in registers
   Raw raw;
-  issue_x(0, 0);
-  issue_raw(0, raw);
+  if (producer) {
+    issue_x(0, 0);
+    issue_raw(0, raw);
+  }
   __syncthreads();  // table built (the loads above are waited for by decode)
-  decode(0, raw, 0);
-  if (S > 1) issue_raw(1, raw);
-  __syncthreads();  // x of step 0 (this wave's loads completed by the fence) and weights of step 0
+  if (producer) {
+    decode(0, raw, 0);
+    if (S > 1) issue_raw(1, raw);
+  }
+  __syncthreads();  // x of step 0 (the fence waits for the loads) and weights of step 0
 
-  // loads issued after a step's x loads: bytes + scale (+ bias)
+  // loads a producer issues after a step's x loads: bytes + scale (+ bias)
   constexpr int kRawLoads = IMPLIED ? 2 : 3;
   for (int st = 0; st < S; ++st) {
     const int cur = st & 1, nxt = cur ^ 1;
-    if (st + 1 < S) issue_x(st + 1, nxt);
-    multiply(cur);
-    if (st + 1 < S) decode(st + 1, raw, nxt);
-    // always issued (the last steps reload the last step's bytes, unused),
-    // so that the count of loads after the x loads is fixed
-    issue_raw(min(st + 2, S - 1), raw);
-    // this wave's x loads of step st+1 have landed in LDS (only the loads
-    // issued after them may still be in flight), its weight stores are done;
-    // then every wave is past step st
-    __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)
+    if (!producer) {
+      multiply(cur);
+    } else {
+      if (st + 1 < S) {
+        issue_x(st + 1, nxt);
+        decode(st + 1, raw, nxt);
+      }
+      // always issued (the last steps reload the last step's bytes, unused),
+      // so that the count of loads after the x loads is fixed
+      issue_raw(min(st + 2, S - 1), raw);
+      // this wave's x loads of step st+1 have landed in LDS (only the loads
+      // issued after them may still be in flight), its weight stores are done
+      __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)
+    }
+    // every wave is past step st: buffer cur is free, buffer nxt is full
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  if (producer) return;
 
   // D layout of 16x16x32: lane holds rows 4*(lane/16)+v, column lane%16
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + v;
-        const int n = n0 + wn * 64 + 16 * j + (lane & 15);
+        const int n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
         if (m < p.M && n < p.N) p.y[(size_t)m * p.N + n] = (half_t)acc[i][j][v];
       }
 }

@@ -256,6 +256,27 @@ def test_t5_qmm_matches_wide():
     assert ok, worst
 
 
+# Shapes for which the tile choice takes each tile shape the library has
+# (32x64 is taken by the small cases above): 32x128, 64x64, 128x64, 64x256,
+# 256x64, 256x128 (also with a ragged row count); checked on sampled output
+# columns.
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M,N,K", [(20, 65536, 256), (40, 17408, 256), (80, 17408, 256), (50, 65536, 256),
+                                   (100, 65536, 256), (160, 12288, 256), (600, 17408, 1024)])
+def test_t5_qmm_tile_shapes(gs, M, N, K):
+    inp = make("t5", M, N, K, gs, "t5", seed=23)
+    print(f"qmm tiles gs{gs} M{M} N{N} K{K}", flush=True)
+    y = run_entry("t5_qmm", inp)
+    assert np.all(np.isfinite(y))
+    assert_close(y, inp, rows=_sample_rows(N, 24), what=f"t5_qmm tiles gs{gs} M{M}")
+
+
+def test_t5_qmm_tile_shapes_explicit_bias():
+    inp = make("t5", 300, 16384, 512, 64, "asym", seed=25)
+    y = run_entry("t5_qmm", inp)
+    assert_close(y, inp, rows=_sample_rows(16384, 26), what="t5_qmm tiles asym")
+
+
 @pytest.mark.parametrize("shape", ["gate", "down"])
 def test_t5_qmm_full_size_sampled(shape):
     N, K = synth.PROJECTION_SHAPES[shape]
