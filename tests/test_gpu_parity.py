@@ -277,6 +277,32 @@ def test_t5_qmm_tile_shapes_explicit_bias():
     assert_close(y, inp, rows=_sample_rows(16384, 26), what="t5_qmm tiles asym")
 
 
+# With one-hot activation rows every output is a single fp16 weight times
+# 1.0, accumulated alone in fp32: exact.  Reading back all N x K weights this
+# way checks every code, every K step and every tile of the fused product bit
+# for bit, with enough tiles that two workgroups share a CU (512 and more).
+@pytest.mark.parametrize("M,N,K,gs,variant", [(20, 65536, 256, 64, "t5"), (20, 65536, 256, 128, "t5"),
+                                              (100, 65536, 256, 64, "t5"), (32, 65536, 512, 64, "asym"),
+                                              (300, 16384, 512, 128, "t5"), (600, 17408, 768, 64, "t5")])
+def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
+    import bit_quantized_decode_qmv_amd as bq
+    inp = make("t5", M, N, K, gs, variant, seed=31)
+    codes = oracle.codes_of("t5", inp.w, K, gs)
+    W16 = oracle.dequant_f16(codes, inp.scales, oracle.effective_biases("t5", inp.scales, inp.biases), gs)
+    wd, sd, bd = dev(inp.w), dev(inp.scales), dev(inp.biases)
+    print(f"qmm one-hot gs{gs} M{M} N{N} K{K} {variant}", flush=True)
+    for base in range(0, K, M):
+        ks = np.arange(base, min(base + M, K))
+        x = np.zeros((M, K), np.float16)
+        x[np.arange(len(ks)), ks] = 1.0
+        y = to_np(bq.t5_qmm(dev(x), wd, sd, gs, biases=bd))
+        want = W16[:, ks].T
+        bad = np.argwhere(y[:len(ks)] != want)
+        assert len(bad) == 0, (f"K columns {base}..{base + len(ks) - 1}: {len(bad)} weights differ, e.g. "
+                               + ", ".join(f"W[{n}][{ks[m]}] {y[m, n]!r} != {want[m, n]!r}" for m, n in bad[:6]))
+        assert not y[len(ks):].any()
+
+
 @pytest.mark.parametrize("shape", ["gate", "down"])
 def test_t5_qmm_full_size_sampled(shape):
     N, K = synth.PROJECTION_SHAPES[shape]
