@@ -23,7 +23,7 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
@@ -35,7 +35,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
                 "bq_t5_qmm", "bq_dequant")
-DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check")
+DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack")
 ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
 
 STATUS = {
@@ -78,6 +78,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bq_linear_route.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int)]
     lib.bq_sym_check.restype = ctypes.c_int
     lib.bq_sym_check.argtypes = [vp, vp, i, i, i, i, vp, vp]
+    lib.bq_t5_repack.restype = ctypes.c_int
+    lib.bq_t5_repack.argtypes = [vp, vp, i, i, i, i, vp, vp]
     ver = lib.bq_abi_version()
     if ver != ABI_VERSION:
         raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
@@ -142,6 +144,11 @@ def bq_sym_check(scales, biases, N, K, bits, group_size, flag, stream=None):
     """C entry point bq_sym_check of include/bq.h (flag: device int pointer)."""
     return _raise_if(load_library().bq_sym_check(scales, biases, N, K, bits, group_size, flag, stream),
                      "bq_sym_check")
+
+
+def bq_t5_repack(w, w_t5, N, K, bits, group_size, flag, stream=None):
+    """C entry point bq_t5_repack of include/bq.h (flag: device int pointer)."""
+    return _raise_if(load_library().bq_t5_repack(w, w_t5, N, K, bits, group_size, flag, stream), "bq_t5_repack")
 
 
 # ---------------------------------------------------------------------------
@@ -258,6 +265,22 @@ def sym_check(scales, biases, bits: int, group_size: int) -> bool:
     return bool(flag.item())
 
 
+def t5_repack(w, bits: int, group_size: int, K: int):
+    """t5 bytes of a 1/2-bit code tensor (int32 words [N][K*bits/32]) and
+    whether every code was 0..2 (then the repack is exact); waits for the
+    flag."""
+    torch = _torch()
+    dev = w.device
+    _check(w, "w", torch.int32, dev)
+    N = w.shape[0]
+    if w.dim() != 2 or w.shape[1] * 32 != K * bits:
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected ({N}, {K * bits // 32})")
+    out = torch.empty((N, (K // group_size) * ((group_size + 4) // 5)), dtype=torch.uint8, device=dev)
+    flag = torch.empty(1, dtype=torch.int32, device=dev)
+    bq_t5_repack(w.data_ptr(), out.data_ptr(), N, K, bits, group_size, flag.data_ptr(), _stream_handle(dev))
+    return out, bool(flag.item())
+
+
 class QuantizedWeight:
     """One layer's packed weights: w (int32 words for bits 1/2, uint8 t5
     bytes), fp16 scales [N][K/gs], fp16 biases or None (implied bias).  The
@@ -275,6 +298,21 @@ class QuantizedWeight:
         if self._sym is None:
             self._sym = sym_check(self.scales, self.biases, self.bits, self.group_size)
         return self._sym
+
+
+    def to_t5(self) -> "QuantizedWeight":
+        """The same layer in t5 bytes (bits 1/2 with stored biases and codes
+        0..2 only).  The biases are dropped when every one equals -scale
+        (the t5 implied bias), else kept."""
+        if self.bits == BITS_T5:
+            return self
+        if self.biases is None:
+            raise ValueError("to_t5 needs stored biases (the implied 1/2-bit bias is not -scale)")
+        w5, ternary = t5_repack(self.w, self.bits, self.group_size, self.K)
+        if not ternary:
+            raise ValueError("the layer has code 3, which t5 cannot hold")
+        implied = sym_check(self.scales, self.biases, BITS_T5, self.group_size)
+        return QuantizedWeight(w5, self.scales, None if implied else self.biases, BITS_T5, self.group_size)
 
 
 def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
@@ -310,5 +348,5 @@ __all__ = [
     "LINEAR_SYM", "MAX_WIDE_M", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
     "bq_linear", "bq_linear_route", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
     "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmv", "qmv_sym", "qmv_wide",
-    "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide",
+    "bq_t5_repack", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
 ]

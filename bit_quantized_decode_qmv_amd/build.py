@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libbq.so")
 SOURCES = ["bq_api.hip"]
-HEADERS = ["qmv_kernels.hpp", "dequant_kernels.hpp", "qmm_kernels.hpp"]
+HEADERS = ["qmv_kernels.hpp", "dequant_kernels.hpp", "qmm_kernels.hpp", "sym_kernels.hpp", "repack_kernels.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

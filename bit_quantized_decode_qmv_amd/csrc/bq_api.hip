@@ -10,6 +10,7 @@
 #include "dequant_kernels.hpp"
 #include "qmm_kernels.hpp"
 #include "qmv_kernels.hpp"
+#include "repack_kernels.hpp"
 #include "sym_kernels.hpp"
 
 namespace {
@@ -441,6 +442,35 @@ int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits,
   if (st != BQ_OK) return st;
   const int64_t blocks = std::min<int64_t>((p.n + 255) / 256, 2048);
   return launch(reinterpret_cast<const void*>(&sym_check_kernel), dim3((unsigned)blocks), dim3(256), 0, stream, &p);
+}
+
+int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_size, int* flag, void* stream) {
+  if (!w || !w_t5 || !flag) return BQ_ERR_NULL;
+  if (bits != 1 && bits != 2) return BQ_ERR_BITS;
+  if (group_size != 64 && group_size != 128) return BQ_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % group_size != 0 || K > (1 << 26)) return BQ_ERR_SHAPE;
+  if ((uint64_t)N * (uint64_t)row_bytes_of(2, K, group_size) >= (1ull << 30)) return BQ_ERR_SHAPE;
+  if (K % 256 != 0) return BQ_ERR_ALIGN;
+  if (!aligned(w, 4) || !aligned(w_t5, 4) || !aligned(flag, 4)) return BQ_ERR_ALIGN;
+  RepackParams p{};
+  p.w = static_cast<const uint32_t*>(w);
+  p.out = static_cast<uint32_t*>(w_t5);
+  p.words_per_row = K / 32 * bits;
+  p.dwords_per_row = row_bytes_of(BQ_BITS_T5, K, group_size) / 4;
+  p.total = (int64_t)N * p.dwords_per_row;
+  p.flag = flag;
+  int st = launch(reinterpret_cast<const void*>(&repack_flag_init_kernel), dim3(1), dim3(64), 0, stream, &p);
+  if (st != BQ_OK) return st;
+  const void* fn;
+  if (bits == 1) {
+    fn = group_size == 64 ? reinterpret_cast<const void*>(&t5_repack_kernel<1, 64>)
+                          : reinterpret_cast<const void*>(&t5_repack_kernel<1, 128>);
+  } else {
+    fn = group_size == 64 ? reinterpret_cast<const void*>(&t5_repack_kernel<2, 64>)
+                          : reinterpret_cast<const void*>(&t5_repack_kernel<2, 128>);
+  }
+  const int64_t blocks = std::min<int64_t>((p.total + 255) / 256, 8192);
+  return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
 }
 
 }  // extern "C"

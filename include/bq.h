@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 2
+#define BQ_ABI_VERSION 3
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -175,6 +175,16 @@ int bq_linear_route(int M, int bits, int flags, int* passes);
  * bias read. */
 int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits, int group_size, int* flag,
                  void* stream);
+
+/* t5 repack -- section 二, the t5 format (existing 1/2-bit weights are
+ * repacked into t5 bytes): w holds uint32 code words [N][K*bits/32] (bits 1
+ * or 2, the layout above); w_t5 receives t5 bytes [N][(K/gs)*ceil(gs/5)]
+ * (the layout above).  Scales and biases stay as they are: s*q + b is the
+ * same weight in both formats.  Writes 1 to the device int *flag when every
+ * code is 0, 1 or 2 (the repack is exact), else 0; a code 3 is written as
+ * digit 2.  K must be a multiple of 256 (whole dwords per t5 row); w, w_t5
+ * and flag need 4-byte alignment.  Asynchronous on stream. */
+int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_size, int* flag, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,13 +13,41 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bq.h")
 
 OK, NULL, BITS, GROUP, SHAPE, MRANGE, ALIGN = 0, -1, -2, -3, -4, -5, -6
+HIP_ERR = -7
+
+# The calls below pass fake device addresses and must all be refused by
+# argument validation.  On a machine with a GPU a call that got past
+# validation would launch a kernel on those addresses, so there these tests
+# do not run at all.
+GPU_PRESENT = os.path.exists("/dev/kfd")
+
+
+class _NoLaunch:
+    """The library, with every entry point checked not to have reached a
+    launch: without a GPU a launch returns BQ_ERR_HIP."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name)
+        if not name.startswith("bq_") or name in ("bq_abi_version", "bq_strerror", "bq_linear_route"):
+            return fn
+
+        def checked(*args):
+            st = fn(*args)
+            assert st != HIP_ERR, f"{name}{args} passed validation and tried to launch"
+            return st
+        return checked
 
 
 @pytest.fixture(scope="module")
 def lib():
+    if GPU_PRESENT:
+        pytest.skip("fake-pointer validation tests run only on machines without a GPU")
     if not os.path.exists(bq.LIB_PATH):
         pytest.fail("libbq.so is not built: run __graft_entry__.build() first")
-    return bq.load_library()
+    return _NoLaunch(bq.load_library())
 
 
 def declared_functions():
@@ -37,7 +65,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 2
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 3
 
 
 def test_strerror_covers_every_status(lib):
@@ -129,7 +157,9 @@ def test_m_range(lib, name):
     assert call(lib, name, bits=bits, M=0) == MRANGE
     assert call(lib, name, bits=bits, M=-1) == MRANGE
     wide = name in ("bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv_wide")
-    assert (call(lib, name, bits=bits, M=6) == MRANGE) == wide
+    # M = 6 is valid for the per-row and qmm entry points; a misaligned y
+    # stops those calls after the M check, before any launch
+    assert call(lib, name, bits=bits, M=6, y=PY + 1) == (MRANGE if wide else ALIGN)
 
 
 @pytest.mark.parametrize("name", U_ENTRIES + T5_ENTRIES + ["bq_dequant"])
@@ -242,3 +272,31 @@ def test_sym_check_validates(lib):
     assert lib.bq_sym_check(PS, PB, 8, 200, 2, 64, vp, None) == SHAPE
     assert lib.bq_sym_check(PS + 1, PB, 8, 256, 2, 64, vp, None) == ALIGN
     assert lib.bq_sym_check(PS, PB, 8, 256, 2, 64, vp + 2, None) == ALIGN
+
+
+def test_t5_repack_validates(lib):
+    fp = PX + 64
+    rp = lambda w=PW, o=PY, N=8, K=256, bits=2, gs=64, flag=fp: lib.bq_t5_repack(w, o, N, K, bits, gs, flag, None)
+    assert rp(w=None) == NULL
+    assert rp(o=None) == NULL
+    assert rp(flag=None) == NULL
+    for bits in (0, 3, 4, -1):
+        assert rp(bits=bits) == BITS
+    for gs in (0, 32, 96, 256):
+        assert rp(gs=gs) == GROUP
+    assert rp(N=0) == SHAPE
+    assert rp(K=0) == SHAPE
+    assert rp(K=320, gs=128) == SHAPE
+    assert rp(K=(1 << 26) + 256) == SHAPE
+    assert rp(N=8192, K=1 << 20) == SHAPE      # input rows past 2^30 bytes
+    assert rp(K=192) == ALIGN                  # t5 rows must be whole dwords
+    assert rp(K=384, gs=128) == ALIGN
+    assert rp(w=PW + 2) == ALIGN
+    assert rp(o=PY + 2) == ALIGN
+    assert rp(flag=fp + 2) == ALIGN
+
+
+def test_t5_repack_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="GPU"):
+        bq.t5_repack(torch.zeros(4, 16, dtype=torch.int32), 2, 64, 256)
