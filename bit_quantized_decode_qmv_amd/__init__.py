@@ -23,11 +23,14 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
 T5_QMM_MIN_M = 17
+DTYPE_F16 = 1
+DTYPE_F32 = 2
+SPEC_MAX_DRAFT = 1024
 ROUTES = {1: "qmv_wide", 2: "qmv_sym", 3: "t5_qmv_wide", 4: "t5_qmm"}
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -35,12 +38,13 @@ LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
                 "bq_t5_qmm", "bq_dequant")
-DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack")
+DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack", "bq_spec_verify_workspace",
+                   "bq_spec_decode_verify")
 ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
 
 STATUS = {
     0: "BQ_OK", -1: "BQ_ERR_NULL", -2: "BQ_ERR_BITS", -3: "BQ_ERR_GROUP", -4: "BQ_ERR_SHAPE",
-    -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP", -8: "BQ_ERR_FLAGS",
+    -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP", -8: "BQ_ERR_FLAGS", -9: "BQ_ERR_WORKSPACE",
 }
 
 
@@ -80,6 +84,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bq_sym_check.argtypes = [vp, vp, i, i, i, i, vp, vp]
     lib.bq_t5_repack.restype = ctypes.c_int
     lib.bq_t5_repack.argtypes = [vp, vp, i, i, i, i, vp, vp]
+    lib.bq_spec_verify_workspace.restype = ctypes.c_int
+    lib.bq_spec_verify_workspace.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bq_spec_decode_verify.restype = ctypes.c_int
+    lib.bq_spec_decode_verify.argtypes = [vp, i, vp, i, i, i, vp, vp, vp, vp, ctypes.c_size_t, vp]
     ver = lib.bq_abi_version()
     if ver != ABI_VERSION:
         raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
@@ -149,6 +157,21 @@ def bq_sym_check(scales, biases, N, K, bits, group_size, flag, stream=None):
 def bq_t5_repack(w, w_t5, N, K, bits, group_size, flag, stream=None):
     """C entry point bq_t5_repack of include/bq.h (flag: device int pointer)."""
     return _raise_if(load_library().bq_t5_repack(w, w_t5, N, K, bits, group_size, flag, stream), "bq_t5_repack")
+
+
+def bq_spec_verify_workspace(B, L, V):
+    """Workspace bytes bq_spec_decode_verify needs (host only)."""
+    n = ctypes.c_size_t(0)
+    _raise_if(load_library().bq_spec_verify_workspace(B, L, V, ctypes.byref(n)), "bq_spec_verify_workspace")
+    return n.value
+
+
+def bq_spec_decode_verify(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens, workspace,
+                          workspace_bytes, stream=None):
+    """C entry point bq_spec_decode_verify of include/bq.h (pointers as integers)."""
+    return _raise_if(load_library().bq_spec_decode_verify(logits, logits_dtype, draft, B, L, V, accepted, next_token,
+                                                          target_tokens, workspace, workspace_bytes, stream),
+                     "bq_spec_decode_verify")
 
 
 # ---------------------------------------------------------------------------
@@ -281,6 +304,39 @@ def t5_repack(w, bits: int, group_size: int, K: int):
     return out, bool(flag.item())
 
 
+def spec_decode_verify(logits, draft, workspace=None, targets: bool = True):
+    """Greedy verification of L draft tokens per sequence against the target
+    logits [B][L+1][V] (fp16 or fp32): (accepted [B], next_token [B],
+    target tokens [B][L+1] or None), int32 tensors.  workspace: a zeroed
+    uint8 tensor of at least bq_spec_verify_workspace bytes, reused across
+    calls (each call leaves it zero); allocated here when None."""
+    torch = _torch()
+    dev = logits.device
+    if logits.dtype not in (torch.float16, torch.float32):
+        raise TypeError(f"logits must be float16 or float32, got {logits.dtype}")
+    _check(logits, "logits", logits.dtype, dev)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B][L+1][V]")
+    B, rows, V = logits.shape
+    L = rows - 1
+    _check(draft, "draft", torch.int32, dev)
+    if tuple(draft.shape) != (B, L):
+        raise ValueError(f"draft has shape {tuple(draft.shape)}, expected {(B, L)}")
+    need = bq_spec_verify_workspace(B, L, V)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", torch.uint8, dev)
+    accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    tgt = torch.empty((B, rows), dtype=torch.int32, device=dev) if targets else None
+    bq_spec_decode_verify(logits.data_ptr(), DTYPE_F16 if logits.dtype == torch.float16 else DTYPE_F32,
+                          draft.data_ptr() if L > 0 else None, B, L, V, accepted.data_ptr(), nxt.data_ptr(),
+                          tgt.data_ptr() if tgt is not None else None, workspace.data_ptr(), workspace.numel(),
+                          _stream_handle(dev))
+    return accepted, nxt, tgt
+
+
 class QuantizedWeight:
     """One layer's packed weights: w (int32 words for bits 1/2, uint8 t5
     bytes), fp16 scales [N][K/gs], fp16 biases or None (implied bias).  The
@@ -348,5 +404,6 @@ __all__ = [
     "LINEAR_SYM", "MAX_WIDE_M", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
     "bq_linear", "bq_linear_route", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
     "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmv", "qmv_sym", "qmv_wide",
-    "bq_t5_repack", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
+    "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_verify_workspace",
+    "bq_t5_repack", "spec_decode_verify", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
 ]

@@ -11,6 +11,7 @@
 #include "qmm_kernels.hpp"
 #include "qmv_kernels.hpp"
 #include "repack_kernels.hpp"
+#include "spec_kernels.hpp"
 #include "sym_kernels.hpp"
 
 namespace {
@@ -73,6 +74,10 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
   return BQ_OK;
 }
+
+// spec verify workspace: row keys, then per-sequence counters
+size_t spec_keys_bytes(int B, int L) { return ((size_t)B * (L + 1) * 8 + 255) / 256 * 256; }
+size_t spec_workspace_bytes(int B, int L) { return spec_keys_bytes(B, L) + (size_t)B * 4; }
 
 int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, void* params) {
   void* args[] = {params};
@@ -306,7 +311,8 @@ const char* bq_strerror(int status) {
   switch (status) {
     case BQ_OK: return "success";
     case BQ_ERR_NULL: return "a required pointer is NULL";
-    case BQ_ERR_BITS: return "bits is not valid for this entry point (1, 2, or BQ_BITS_T5 = 0)";
+    case BQ_ERR_BITS:
+      return "bits (1, 2, or BQ_BITS_T5 = 0) or the logits dtype is not valid for this entry point";
     case BQ_ERR_GROUP: return "group_size must be 64 or 128";
     case BQ_ERR_SHAPE:
       return "N and K must be positive, K a multiple of group_size, and the sizes within the limits of bq.h";
@@ -316,6 +322,7 @@ const char* bq_strerror(int status) {
              "call has K not a multiple of 256";
     case BQ_ERR_FLAGS: return "flags holds bits this entry point does not define";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case BQ_ERR_WORKSPACE: return "the workspace is NULL or smaller than bq_spec_verify_workspace reports";
   }
   return "unknown bq status";
 }
@@ -471,6 +478,43 @@ int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_si
   }
   const int64_t blocks = std::min<int64_t>((p.total + 255) / 256, 8192);
   return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
+}
+
+int bq_spec_verify_workspace(int B, int L, int V, size_t* bytes) {
+  if (!bytes) return BQ_ERR_NULL;
+  if (B < 1 || L < 0 || L > BQ_SPEC_MAX_DRAFT || V < 1) return BQ_ERR_SHAPE;
+  *bytes = spec_workspace_bytes(B, L);
+  return BQ_OK;
+}
+
+int bq_spec_decode_verify(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
+                          int* accepted, int* next_token, int* target_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!logits || (L > 0 && !draft) || !accepted || !next_token) return BQ_ERR_NULL;
+  if (logits_dtype != BQ_DTYPE_F16 && logits_dtype != BQ_DTYPE_F32) return BQ_ERR_BITS;
+  if (B < 1 || L < 0 || L > BQ_SPEC_MAX_DRAFT || V < 1) return BQ_ERR_SHAPE;
+  const int64_t chunks = (V + kSpecChunk - 1) / kSpecChunk;
+  if ((int64_t)B * (L + 1) * chunks >= (1ll << 31)) return BQ_ERR_SHAPE;
+  if (!workspace || workspace_bytes < spec_workspace_bytes(B, L)) return BQ_ERR_WORKSPACE;
+  const size_t esz = logits_dtype == BQ_DTYPE_F16 ? 2 : 4;
+  if (!aligned(logits, esz) || (draft && !aligned(draft, 4)) || !aligned(accepted, 4) ||
+      !aligned(next_token, 4) || (target_tokens && !aligned(target_tokens, 4)) || !aligned(workspace, 8))
+    return BQ_ERR_ALIGN;
+  SpecParams p{};
+  p.logits = logits;
+  p.draft = draft;
+  p.accepted = accepted;
+  p.next_token = next_token;
+  p.target = target_tokens;
+  p.keys = static_cast<unsigned long long*>(workspace);
+  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + spec_keys_bytes(B, L));
+  p.B = B;
+  p.L = L;
+  p.V = V;
+  p.chunks = (int)chunks;
+  const void* fn = logits_dtype == BQ_DTYPE_F16 ? reinterpret_cast<const void*>(&spec_verify_kernel<_Float16>)
+                                                : reinterpret_cast<const void*>(&spec_verify_kernel<float>);
+  return launch(fn, dim3((unsigned)((int64_t)B * (L + 1) * chunks)), dim3(kSpecThreads), 0, stream, &p);
 }
 
 }  // extern "C"

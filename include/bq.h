@@ -54,18 +54,20 @@
 #ifndef BQ_H
 #define BQ_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 3
+#define BQ_ABI_VERSION 4
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
 typedef enum bq_status {
   BQ_OK = 0,
   BQ_ERR_NULL = -1,       /* a required pointer is NULL */
-  BQ_ERR_BITS = -2,       /* bits not valid for this entry point */
+  BQ_ERR_BITS = -2,       /* bits (or the logits dtype) not valid for this entry point */
   BQ_ERR_GROUP = -3,      /* group_size not 64 or 128 */
   BQ_ERR_SHAPE = -4,      /* N or K not positive, K % group_size != 0, K > 2^26,
                              or N * (packed row bytes) >= 2^30, or
@@ -75,7 +77,8 @@ typedef enum bq_status {
   BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
   BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
   BQ_ERR_HIP = -7,        /* the HIP runtime rejected a launch */
-  BQ_ERR_FLAGS = -8       /* bq_linear: flags holds undefined bits */
+  BQ_ERR_FLAGS = -8,      /* bq_linear: flags holds undefined bits */
+  BQ_ERR_WORKSPACE = -9   /* bq_spec_decode_verify: workspace NULL or too small */
 } bq_status;
 
 /* bq_linear flags */
@@ -185,6 +188,38 @@ int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits,
  * digit 2.  K must be a multiple of 256 (whole dwords per t5 row); w, w_t5
  * and flag need 4-byte alignment.  Asynchronous on stream. */
 int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_size, int* flag, void* stream);
+
+/* speculative-decoding verification -- section 三 (spec_decode_verify:
+ * comparing the draft tokens, counting the accepted length and producing the
+ * correction token, fused into one kernel).  For each sequence b:
+ *   t[i] = argmax over v of logits[b][i][v], i = 0..L (the largest value;
+ *          equal values: the lowest v; -0 equals +0; a NaN is larger than
+ *          every number and the first NaN wins);
+ *   accepted[b] = the first i < L with draft[b][i] != t[i], else L;
+ *   next_token[b] = t[accepted[b]] (the correction token, or the bonus token
+ *          when every draft token is accepted);
+ *   target_tokens[b][i] = t[i] when target_tokens is not NULL.
+ * logits: [B][L+1][V] row-major, fp16 (BQ_DTYPE_F16) or fp32 (BQ_DTYPE_F32),
+ * aligned to its element size; draft: int32 [B][L] (may be NULL when L = 0);
+ * accepted, next_token: int32 [B]; target_tokens: int32 [B][L+1] or NULL;
+ * all device memory owned by the caller, int arrays 4-byte aligned.
+ * 1 <= B, 0 <= L <= BQ_SPEC_MAX_DRAFT, 1 <= V.
+ * workspace: device memory of at least bq_spec_verify_workspace() bytes,
+ * 8-byte aligned, all zero before its first use (e.g. hipMemset once);
+ * every call leaves it zero again.  Calls that overlap in time on one
+ * workspace race; give concurrent streams their own.  The library
+ * allocates nothing.  Asynchronous on stream; one kernel launch. */
+#define BQ_DTYPE_F16 1
+#define BQ_DTYPE_F32 2
+#define BQ_SPEC_MAX_DRAFT 1024
+
+/* Workspace bytes bq_spec_decode_verify needs for B sequences of L draft
+ * tokens (into *bytes).  Host-only. */
+int bq_spec_verify_workspace(int B, int L, int V, size_t* bytes);
+
+int bq_spec_decode_verify(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
+                          int* accepted, int* next_token, int* target_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

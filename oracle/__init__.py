@@ -10,3 +10,4 @@ from .qmv_oracle import (T5_MAX_BYTE, abs_mass, algorithmic_bytes, bits_of, chec
                          qmv_brute, qmv_exact, qmv_f64, qmv_reference, sym_ratio, t5_group_bytes,
                          t5_pack, t5_unpack, t5_unpack_scalar, tolerance, unpack_words,
                          unpack_words_scalar, weights_f64)
+from .spec_oracle import spec_verify, spec_verify_scalar, target_tokens

@@ -9,3 +9,4 @@ __all__ = [
     "draw_biases", "draw_scales", "draw_t5_bytes", "draw_words", "draw_x", "make_inputs",
     "packed_row_bytes", "seed_for", "t5_bytes_per_group",
 ]
+from .spec import QWEN_VOCAB, SpecInputs, make_spec_inputs

@@ -31,7 +31,8 @@ class _NoLaunch:
 
     def __getattr__(self, name):
         fn = getattr(self._lib, name)
-        if not name.startswith("bq_") or name in ("bq_abi_version", "bq_strerror", "bq_linear_route"):
+        if not name.startswith("bq_") or name in ("bq_abi_version", "bq_strerror", "bq_linear_route",
+                                                  "bq_spec_verify_workspace"):
             return fn
 
         def checked(*args):
@@ -65,12 +66,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 3
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 4
 
 
 def test_strerror_covers_every_status(lib):
-    msgs = {s: bq.strerror(s) for s in range(-8, 1)}
-    assert len(set(msgs.values())) == 9
+    msgs = {s: bq.strerror(s) for s in range(-9, 1)}
+    assert len(set(msgs.values())) == 10
     assert bq.strerror(-99) == "unknown bq status"
 
 
@@ -300,3 +301,47 @@ def test_t5_repack_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="GPU"):
         bq.t5_repack(torch.zeros(4, 16, dtype=torch.int32), 2, 64, 256)
+
+
+WORKSPACE_ERR = -9
+
+
+def test_spec_workspace_size(lib):
+    import ctypes
+    n = ctypes.c_size_t(0)
+    assert lib.bq_spec_verify_workspace(4, 7, 151936, ctypes.byref(n)) == OK
+    assert n.value >= 4 * 8 * 8 + 4 * 4
+    assert bq.bq_spec_verify_workspace(4, 7, 151936) == n.value
+    assert lib.bq_spec_verify_workspace(0, 7, 100, ctypes.byref(n)) == SHAPE
+    assert lib.bq_spec_verify_workspace(1, -1, 100, ctypes.byref(n)) == SHAPE
+    assert lib.bq_spec_verify_workspace(1, 1025, 100, ctypes.byref(n)) == SHAPE
+    assert lib.bq_spec_verify_workspace(1, 1, 0, ctypes.byref(n)) == SHAPE
+    assert lib.bq_spec_verify_workspace(1, 1, 1, None) == NULL
+
+
+def test_spec_verify_validates(lib):
+    D, A, T, W = PX, PW, PS, PB  # fake, aligned addresses
+    big = 1 << 20
+
+    def sv(lg=PY, dt=1, d=D, B=2, L=3, V=1000, a=A, n=A + 64, t=T, w=W, wb=big):
+        return lib.bq_spec_decode_verify(lg, dt, d, B, L, V, a, n, t, w, wb, None)
+    assert sv(lg=None) == NULL
+    assert sv(d=None) == NULL
+    assert sv(a=None) == NULL
+    assert sv(n=None) == NULL
+    for dt in (0, 3, -1):
+        assert sv(dt=dt) == BITS
+    assert sv(B=0) == SHAPE
+    assert sv(L=-1) == SHAPE
+    assert sv(L=1025) == SHAPE
+    assert sv(V=0) == SHAPE
+    assert sv(B=1 << 20, L=1000, V=1 << 20) == SHAPE     # grid past 2^31 workgroups
+    assert sv(w=None) == WORKSPACE_ERR
+    assert sv(wb=16) == WORKSPACE_ERR
+    assert sv(lg=PY + 1) == ALIGN
+    assert sv(lg=PY + 2, dt=2) == ALIGN                   # fp32 logits need 4 bytes
+    assert sv(d=D + 2) == ALIGN
+    assert sv(a=A + 2) == ALIGN
+    assert sv(n=A + 66) == ALIGN
+    assert sv(t=T + 2) == ALIGN
+    assert sv(w=W + 4) == ALIGN
