@@ -23,21 +23,23 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 4
+ABI_VERSION = 6
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
 T5_QMM_MIN_M = 17
+QMM_MIN_M = 17
+QMM_MIN_TILES = 128
 DTYPE_F16 = 1
 DTYPE_F32 = 2
 SPEC_MAX_DRAFT = 1024
-ROUTES = {1: "qmv_wide", 2: "qmv_sym", 3: "t5_qmv_wide", 4: "t5_qmm"}
+ROUTES = {1: "qmv_wide", 2: "qmv_sym", 3: "t5_qmv_wide", 4: "t5_qmm", 5: "qmm"}
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
-                "bq_t5_qmm", "bq_dequant")
+                "bq_t5_qmm", "bq_dequant", "bq_qmm")
 DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack", "bq_spec_verify_workspace",
                    "bq_spec_decode_verify")
 ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
@@ -79,7 +81,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bq_linear.restype = ctypes.c_int
     lib.bq_linear.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.bq_linear_route.restype = ctypes.c_int
-    lib.bq_linear_route.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.bq_linear_route.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int)]
     lib.bq_sym_check.restype = ctypes.c_int
     lib.bq_sym_check.argtypes = [vp, vp, i, i, i, i, vp, vp]
     lib.bq_t5_repack.restype = ctypes.c_int
@@ -123,6 +125,7 @@ bq_t5_qmv = _c_entry("bq_t5_qmv")
 bq_t5_qmv_wide = _c_entry("bq_t5_qmv_wide")
 bq_t5_qmm = _c_entry("bq_t5_qmm")
 bq_dequant = _c_entry("bq_dequant")
+bq_qmm = _c_entry("bq_qmm")
 
 
 def bq_abi_version() -> int:
@@ -141,10 +144,10 @@ def bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags, stream=
                                                stream), "bq_linear")
 
 
-def bq_linear_route(M, bits, flags=0):
-    """(route name, passes) bq_linear takes for (M, bits, flags); host only."""
+def bq_linear_route(M, N, bits, flags=0):
+    """(route name, passes) bq_linear takes for (M, N, bits, flags); host only."""
     passes = ctypes.c_int(0)
-    st = _raise_if(load_library().bq_linear_route(M, bits, flags, ctypes.byref(passes)), "bq_linear_route")
+    st = _raise_if(load_library().bq_linear_route(M, N, bits, flags, ctypes.byref(passes)), "bq_linear_route")
     return ROUTES[st], passes.value
 
 
@@ -266,6 +269,13 @@ def t5_qmm(x, w, scales, group_size: int, biases=None, out=None):
     return _run("bq_t5_qmm", x, w, scales, biases, BITS_T5, group_size, out, M, N, K, (M, N))
 
 
+def qmm(x, w, scales, bits: int, group_size: int, biases=None, out=None):
+    """Fused 1/2-bit prefill product y = x . W^T (biases None: implied
+    -scale*(2^bits-1)/2)."""
+    M, N, K = _shapes(x, scales, group_size)
+    return _run("bq_qmm", x, w, scales, biases, bits, group_size, out, M, N, K, (M, N))
+
+
 def dequant(w, scales, biases, bits: int, group_size: int, K: int, out=None):
     """fp16 [N][K] weights, each the correctly rounded scale*q + bias."""
     N = scales.shape[0]
@@ -373,8 +383,10 @@ class QuantizedWeight:
 
 def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
     """y = x . W^T for any number of rows, routed as bq_linear does (bits
-    1/2: passes of up to 5 rows through the wide or symmetric kernel; t5:
-    wide passes below T5_QMM_MIN_M rows, the fused qmm from there).  sym
+    1/2: the fused qmm from QMM_MIN_M rows when the product has
+    QMM_MIN_TILES tiles, else passes of up to 5 rows through the wide or
+    symmetric kernel; t5: wide passes below T5_QMM_MIN_M rows, the fused
+    qmm from there).  sym
     defaults to the layer's checked symmetric-bias property."""
     use_sym = qw.sym if sym is None else sym
     M, K = x.shape
@@ -401,9 +413,9 @@ def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
 
 __all__ = [
     "ABI_VERSION", "ALL_SYMBOLS", "BITS_T5", "BQError", "DISPATCH_POINTS", "ENTRY_POINTS", "LIB_PATH",
-    "LINEAR_SYM", "MAX_WIDE_M", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
-    "bq_linear", "bq_linear_route", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
-    "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmv", "qmv_sym", "qmv_wide",
+    "LINEAR_SYM", "MAX_WIDE_M", "QMM_MIN_M", "QMM_MIN_TILES", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
+    "bq_linear", "bq_linear_route", "bq_qmm", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
+    "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmm", "qmv", "qmv_sym", "qmv_wide",
     "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_verify_workspace",
     "bq_t5_repack", "spec_decode_verify", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
 ]

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "bq.h"
 #include "dequant_kernels.hpp"
@@ -27,7 +28,7 @@ static_assert(sb_vectors(bq::kR, kMaxDecodeGroups) <= bq::kSbRounds * bq::kThrea
                   sb_vectors(bq::kR, kMaxDecodeGroups + 1) > bq::kSbRounds * bq::kThreads,
               "decode group limit");
 
-enum Entry { E_QMV, E_WIDE, E_SYM, E_T5, E_T5_WIDE, E_QMM, E_DEQUANT };
+enum Entry { E_QMV, E_WIDE, E_SYM, E_T5, E_T5_WIDE, E_QMM, E_DEQUANT, E_UQMM };
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -55,9 +56,10 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if ((uint64_t)N * (uint64_t)row_bytes_of(bits == BQ_BITS_T5 ? BQ_BITS_T5 : 2, K, gs) >= (1ull << 30) ||
       (uint64_t)N * (uint64_t)(K / gs) >= (1ull << 29))
     return BQ_ERR_SHAPE;
-  if (e != E_DEQUANT && e != E_QMM && K / gs > kMaxDecodeGroups) return BQ_ERR_SHAPE;
+  const bool mm = (e == E_QMM || e == E_UQMM);
+  if (e != E_DEQUANT && !mm && K / gs > kMaxDecodeGroups) return BQ_ERR_SHAPE;
   // qmm addresses x with 32-bit offsets too
-  if (e == E_QMM && M > 0 && (uint64_t)M * (uint64_t)K * 2 >= (1ull << 31)) return BQ_ERR_SHAPE;
+  if (mm && M > 0 && (uint64_t)M * (uint64_t)K * 2 >= (1ull << 31)) return BQ_ERR_SHAPE;
   if (e != E_DEQUANT) {
     if (M < 1) return BQ_ERR_M;
     if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
@@ -68,7 +70,7 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
   if (bits == BQ_BITS_T5 && K % 256 != 0) return BQ_ERR_ALIGN;
   if (e != E_DEQUANT && !aligned(x, 16)) return BQ_ERR_ALIGN;
   // the decode kernels read scales and biases in 16-byte vectors
-  if (e != E_DEQUANT && e != E_QMM &&
+  if (e != E_DEQUANT && !mm &&
       (!aligned(scales, 16) || (biases && e != E_SYM && !aligned(biases, 16))))
     return BQ_ERR_ALIGN;
   if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
@@ -218,40 +220,49 @@ int run_qmv(Entry e, const void* x, const void* w, const void* scales, const voi
   return BQ_OK;
 }
 
-// ---------------------------------------------------------------- t5 qmm
-template <int BM, int BN, int GS, bool IMPLIED>
+// ---------------------------------------------------------------- qmm
+// the decoder of a format: t5 bytes (bits = BQ_BITS_T5) or 1/2-bit words
+template <int BN, int BITS, int GS, bool IMPLIED>
+using QmmDecoder = typename std::conditional<BITS == BQ_BITS_T5, T5Decoder<BN, GS, IMPLIED>,
+                                             UqDecoder<BN, (BITS == 1 ? 1 : 2), GS, IMPLIED>>::type;
+
+template <int BM, int BN, int BITS, int GS, bool IMPLIED>
 int launch_qmm_t(const QmmParams& p, void* stream) {
-  const void* fn = reinterpret_cast<const void*>(&t5_qmm_kernel<BM, BN, GS, IMPLIED>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)qmm_lds_bytes(BM, BN));
+  typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
+  const void* fn = reinterpret_cast<const void*>(&qmm_kernel<BM, BN, Dec>);
+  const size_t lds = qmm_lds_bytes(BM, BN, Dec::kLutWords);
+  static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
   dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   QmmParams q = p;
-  return launch(fn, grid, dim3(kQmmThreads), qmm_lds_bytes(BM, BN), stream, &q);
+  return launch(fn, grid, dim3(kQmmThreads), lds, stream, &q);
 }
 
 // Estimated cycles of one call with BM x BN tiles: per K step the larger of
 // the MFMA cycles and the LDS cycles (operand reads, tile writes), plus the
-// weight-decoding ALU cycles (measured not to overlap the MFMAs), times the
-// rounds of workgroups over 256 CUs; against the L2 / last-level-cache
-// traffic of re-reading x once per column of tiles and W once per row of
-// tiles at 32 bytes per clock per CU.  Only the order of the estimates
-// matters: it picks the tile shape.
-double qmm_cost(int M, int N, int K, int BM, int BN) {
+// weight-decoding ALU cycles (measured not to overlap the MFMAs; alu_per_col
+// per weight row of the tile), times the rounds of workgroups over 256 CUs;
+// against the L2 / last-level-cache traffic of re-reading x once per column
+// of tiles and W (w_bytes_per_weight) once per row of tiles at 32 bytes per
+// clock per CU.  Only the order of the estimates matters: it picks the tile
+// shape.
+double qmm_cost(int M, int N, int K, int BM, int BN, int lut_words, double alu_per_col,
+                double w_bytes_per_weight) {
   const double mfma = (double)BM * BN / 32.0;
   const double lds = 64.0 * (BM / 32 + BN / 32) + (BM + BN);
-  const double alu = 2.5 * BN;
+  const double alu = alu_per_col * BN;
   const double step = std::max(mfma, lds) + alu;
   const double tiles = (double)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-  const int per_cu = qmm_lds_bytes(BM, BN) * 2 <= 160 * 1024 ? 2 : 1;
+  const int per_cu = qmm_lds_bytes(BM, BN, lut_words) * 2 <= 160 * 1024 ? 2 : 1;
   const double rounds = std::ceil(tiles / (256.0 * per_cu));
   const double compute = rounds * per_cu * (K / kQmmBK) * step;
-  const double traffic = ((double)M * K * 2 * ((N + BN - 1) / BN) + (double)N * K * 0.2 * ((M + BM - 1) / BM)) /
+  const double traffic = ((double)M * K * 2 * ((N + BN - 1) / BN) +
+                          (double)N * K * w_bytes_per_weight * ((M + BM - 1) / BM)) /
                          (256.0 * 32.0);
   return std::max(compute, traffic);
 }
 
-template <int GS, bool IMPLIED>
+template <int BITS, int GS, bool IMPLIED>
 int launch_qmm_m(const QmmParams& p, void* stream) {
   typedef int (*Fn)(const QmmParams&, void*);
   struct Cand {
@@ -262,16 +273,19 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
   // (128 x 256 tiles, which it picks for a few, do not fit the registers of
   // the two wave kinds)
   static const Cand cands[] = {
-      {32, 64, &launch_qmm_t<32, 64, GS, IMPLIED>},     {32, 128, &launch_qmm_t<32, 128, GS, IMPLIED>},
-      {64, 64, &launch_qmm_t<64, 64, GS, IMPLIED>},     {64, 256, &launch_qmm_t<64, 256, GS, IMPLIED>},
-      {128, 64, &launch_qmm_t<128, 64, GS, IMPLIED>},   {256, 64, &launch_qmm_t<256, 64, GS, IMPLIED>},
-      {256, 128, &launch_qmm_t<256, 128, GS, IMPLIED>},
+      {32, 64, &launch_qmm_t<32, 64, BITS, GS, IMPLIED>},   {32, 128, &launch_qmm_t<32, 128, BITS, GS, IMPLIED>},
+      {64, 64, &launch_qmm_t<64, 64, BITS, GS, IMPLIED>},   {64, 256, &launch_qmm_t<64, 256, BITS, GS, IMPLIED>},
+      {128, 64, &launch_qmm_t<128, 64, BITS, GS, IMPLIED>}, {256, 64, &launch_qmm_t<256, 64, BITS, GS, IMPLIED>},
+      {256, 128, &launch_qmm_t<256, 128, BITS, GS, IMPLIED>},
   };
+  const int lut_words = QmmDecoder<64, BITS, GS, IMPLIED>::kLutWords;
+  const double alu = BITS == BQ_BITS_T5 ? 2.5 : 1.5;
+  const double wbytes = BITS == BQ_BITS_T5 ? 0.2 : BITS / 8.0;
   const Cand* best = nullptr;
   double best_cost = 0.0;
   for (const Cand& c : cands) {
     if (c.bm > 32 && c.bm / 2 >= p.M) continue;  // a tile at least half full of rows
-    const double cost = qmm_cost(p.M, p.N, p.K, c.bm, c.bn);
+    const double cost = qmm_cost(p.M, p.N, p.K, c.bm, c.bn, lut_words, alu, wbytes);
     if (!best || cost < best_cost) {
       best = &c;
       best_cost = cost;
@@ -280,8 +294,15 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
   return best->fn(p, stream);
 }
 
+template <int BITS>
+int launch_qmm_bits(const QmmParams& p, int group_size, bool implied, void* stream) {
+  if (group_size == 64)
+    return implied ? launch_qmm_m<BITS, 64, true>(p, stream) : launch_qmm_m<BITS, 64, false>(p, stream);
+  return implied ? launch_qmm_m<BITS, 128, true>(p, stream) : launch_qmm_m<BITS, 128, false>(p, stream);
+}
+
 int launch_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
-               int K, int group_size, void* stream) {
+               int K, int bits, int group_size, void* stream) {
   QmmParams p{};
   p.x = static_cast<const half_t*>(x);
   p.w = static_cast<const uint8_t*>(w);
@@ -292,13 +313,14 @@ int launch_qmm(const void* x, const void* w, const void* scales, const void* bia
   p.N = N;
   p.K = K;
   p.G = K / group_size;
-  p.row_bytes = row_bytes_of(BQ_BITS_T5, K, group_size);
+  p.row_bytes = row_bytes_of(bits, K, group_size);
   p.x_bytes = (int)((size_t)M * K * 2);
   p.w_bytes = (int)((size_t)N * p.row_bytes);
   p.sb_bytes = (int)((size_t)N * p.G * 2);
   const bool implied = biases == nullptr;
-  if (group_size == 64) return implied ? launch_qmm_m<64, true>(p, stream) : launch_qmm_m<64, false>(p, stream);
-  return implied ? launch_qmm_m<128, true>(p, stream) : launch_qmm_m<128, false>(p, stream);
+  if (bits == BQ_BITS_T5) return launch_qmm_bits<BQ_BITS_T5>(p, group_size, implied, stream);
+  if (bits == 1) return launch_qmm_bits<1>(p, group_size, implied, stream);
+  return launch_qmm_bits<2>(p, group_size, implied, stream);
 }
 
 }  // namespace
@@ -352,11 +374,18 @@ int bq_t5_qmv_wide(const void* x, const void* w, const void* scales, const void*
   return run_qmv(E_T5_WIDE, x, w, scales, biases, y, M, N, K, bits, group_size, stream);
 }
 
+int bq_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
+           int K, int bits, int group_size, void* stream) {
+  int st = validate(E_UQMM, x, w, scales, biases, y, M, N, K, bits, group_size);
+  if (st != BQ_OK) return st;
+  return launch_qmm(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
 int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
               int N, int K, int bits, int group_size, void* stream) {
   int st = validate(E_QMM, x, w, scales, biases, y, M, N, K, bits, group_size);
   if (st != BQ_OK) return st;
-  return launch_qmm(x, w, scales, biases, y, M, N, K, group_size, stream);
+  return launch_qmm(x, w, scales, biases, y, M, N, K, BQ_BITS_T5, group_size, stream);
 }
 
 int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
@@ -395,13 +424,16 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
   return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
 }
 
-int bq_linear_route(int M, int bits, int flags, int* passes) {
+int bq_linear_route(int M, int N, int bits, int flags, int* passes) {
   if (M < 1) return BQ_ERR_M;
+  if (N < 1) return BQ_ERR_SHAPE;
   if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
-  int route, n;
+  int route, n = 1;
   if (bits == BQ_BITS_T5 && M >= BQ_T5_QMM_MIN_M) {
     route = BQ_ROUTE_T5_QMM;
-    n = 1;
+  } else if (bits != BQ_BITS_T5 && M >= BQ_QMM_MIN_M &&
+             (int64_t)((N + 63) / 64) * ((M + 31) / 32) >= BQ_QMM_MIN_TILES) {
+    route = BQ_ROUTE_QMM;
   } else {
     route = bits == BQ_BITS_T5 ? BQ_ROUTE_T5_WIDE : ((flags & BQ_LINEAR_SYM) ? BQ_ROUTE_QMV_SYM : BQ_ROUTE_QMV_WIDE);
     n = (M + BQ_MAX_WIDE_M - 1) / BQ_MAX_WIDE_M;
@@ -414,11 +446,16 @@ int bq_linear(const void* x, const void* w, const void* scales, const void* bias
               int K, int bits, int group_size, int flags, void* stream) {
   if ((flags & ~BQ_LINEAR_SYM) != 0) return BQ_ERR_FLAGS;
   int passes = 0;
-  const int route = bq_linear_route(M, bits, flags, &passes);
+  const int route = bq_linear_route(M, N, bits, flags, &passes);
   if (route < 0) return route;
   // symmetric: the bias is implied and never read (t5: -scale)
   const void* b = (flags & BQ_LINEAR_SYM) ? nullptr : biases;
   if (route == BQ_ROUTE_T5_QMM) return bq_t5_qmm(x, w, scales, b, y, M, N, K, bits, group_size, stream);
+  if (route == BQ_ROUTE_QMM) {
+    // without the symmetric flag the stored biases are required, as for the wide route
+    if (!b && !(flags & BQ_LINEAR_SYM)) return BQ_ERR_NULL;
+    return bq_qmm(x, w, scales, b, y, M, N, K, bits, group_size, stream);
+  }
   const Entry e = route == BQ_ROUTE_T5_WIDE ? E_T5_WIDE : (route == BQ_ROUTE_QMV_SYM ? E_SYM : E_WIDE);
   // every pass is validated in full before it launches; the first check
   // also covers the arguments common to all passes

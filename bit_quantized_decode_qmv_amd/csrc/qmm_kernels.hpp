@@ -1,9 +1,11 @@
-// t5 prefill product on the matrix cores: y[M][N] = x[M][K] . W^T with W
-// unpacked from t5 bytes tile by tile.
+// Prefill products on the matrix cores: y[M][N] = x[M][K] . W^T with W
+// unpacked tile by tile, from t5 bytes or from 1/2-bit uint32 codes.
 //
 // Method: "oMLX Bonsai 自定义内核" article, section 二 path 3 -- for prefill
 // with more than 16 rows the t5 weights go through a fused "unpack + matrix
-// multiply" kernel that reads each t5 byte once per weight tile.
+// multiply" kernel that reads each t5 byte once per weight tile.  The same
+// pipeline with a decoder for uint32 codes replaces section 二 path 1's
+// 1-bit prefill (dequantize to float16, then a matrix multiply).
 //
 // gfx950 design
 // -------------
@@ -55,8 +57,8 @@ struct QmmParams {
 constexpr int kQmmBK = 64;        // codes per K step
 constexpr int kQmmThreads = 512;  // 4 MFMA waves (2 x 2 over the tile) + 4 loading/decoding waves
 
-constexpr size_t qmm_lds_bytes(int BM, int BN) {
-  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * BN * kQmmBK * 2 + 256 * 4;
+constexpr size_t qmm_lds_bytes(int BM, int BN, int lut_words) {
+  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * BN * kQmmBK * 2 + (size_t)lut_words * 4;
 }
 
 // 16-byte unit (row, q) of a 128-byte LDS row
@@ -142,16 +144,177 @@ __device__ __forceinline__ void t5_decode_h(int h, const uint32_t (&wv)[4], uint
   }
 }
 
-template <int BM, int BN, int GS, bool IMPLIED>
-__global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
+
+// ---------------------------------------------------------------------------
+// Decoders.  A producer thread owns NC = BN/4 codes of one weight row per K
+// step (codes 64*step + NC*h .. +NC-1; h is the same for a whole wave).  A
+// decoder loads their packed bytes and the group's scale (and bias) one step
+// ahead (issue), and turns them into NC/2 dwords of fp16 pairs, codes
+// (2t, 2t+1) in dword t (decode).  kRawLoads is the number of loads issue
+// makes, for the pipeline's vmcnt bookkeeping; kLutWords the size of the
+// decoder's LDS table.
+// ---------------------------------------------------------------------------
+template <int BN, int GS, bool IMPLIED>
+struct T5Decoder {
+  static constexpr int NC = BN / 4;
+  static constexpr int kRawLoads = IMPLIED ? 2 : 3;
+  static constexpr int kLutWords = 256;
+  static constexpr int P1 = GS == 128 ? 1 : 0;
+  struct Raw {
+    u32x4 d;
+    uint16_t s, b;
+  };
+  rsrc_t rw, rs, rb;
+  uint32_t row_off, sb_row;
+  int h;
+
+  __device__ __forceinline__ static void init_lut(uint32_t* lut, int tid) {
+    if (tid < 256) lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
+  }
+  __device__ __forceinline__ T5Decoder(const QmmParams& p, int n, int h_) : h(h_) {
+    rw = make_rsrc(p.w, p.w_bytes);
+    rs = make_rsrc(p.s, p.sb_bytes);
+    rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
+    row_off = (uint32_t)n * (uint32_t)p.row_bytes;
+    sb_row = (uint32_t)n * (uint32_t)p.G;
+  }
+  __device__ __forceinline__ int group_base(int step) const { return GS == 64 ? 13 * step : 26 * (step >> 1); }
+  __device__ __forceinline__ int span_start(int step) const {
+    const int par = GS == 128 ? (step & 1) : 0;
+    return par == 0 ? t5_span_start<GS, 0, NC>(h) : t5_span_start<GS, P1, NC>(h);
+  }
+  __device__ __forceinline__ void issue(int step, Raw& rw_) const {
+    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
+    // 16 bytes from the dword at or below the span's first byte: a span has
+    // at most 13 bytes (14 for the second half of a 128-group, which starts
+    // 0 or 2 bytes into its dword), so the window always holds it; dwords
+    // past the end of W read as zeros
+    rw_.d = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(a & ~3u), 0, 0);
+    const uint32_t so = 2u * (sb_row + (uint32_t)((step * kQmmBK) / GS));
+    rw_.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+    if constexpr (!IMPLIED) rw_.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, 0, 0);
+    else rw_.b = 0;
+  }
+  __device__ __forceinline__ void decode(int step, const Raw& rw_, const uint32_t* lut,
+                                         uint32_t (&out)[NC / 2]) const {
+    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
+    const uint32_t sh = a & 3u;
+    uint32_t wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(k < 3 ? rw_.d[k + 1] : 0u, rw_.d[k], sh);
+    uint64_t wt;
+    if constexpr (IMPLIED) {
+      const uint32_t sp = rw_.s, sn = rw_.s ^ 0x8000u;  // +s, -s (exact)
+      wt = (uint64_t)sn | ((uint64_t)sp << 32);
+    } else {
+      const float s = h2f(__builtin_bit_cast(half_t, rw_.s)), b = h2f(__builtin_bit_cast(half_t, rw_.b));
+      const uint32_t v0 = __builtin_bit_cast(uint16_t, affine_to_half(s, 0u, b));
+      const uint32_t v1 = __builtin_bit_cast(uint16_t, affine_to_half(s, 1u, b));
+      const uint32_t v2 = __builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b));
+      wt = (uint64_t)(v0 | (v1 << 16)) | ((uint64_t)v2 << 32);
+    }
+    const int par = GS == 128 ? (step & 1) : 0;
+    if (par == 0) t5_decode_h<GS, 0, NC>(h, wv, wt, lut, out);
+    else t5_decode_h<GS, P1, NC>(h, wv, wt, lut, out);
+  }
+};
+
+// Selector table of the uint32 decoder: for the byte value v (four 2-bit or
+// eight 1-bit codes, LSB first), the v_perm_b32 selectors that place the
+// fp16 weight of each code -- bytes 2q and 2q+1 of the row's weight table --
+// two codes per dword.
+template <int BITS>
+__device__ __forceinline__ uint32_t uq_selector(uint32_t v, int pair) {
+  const uint32_t qa = (v >> (2 * pair * BITS)) & ((1u << BITS) - 1u);
+  const uint32_t qb = (v >> ((2 * pair + 1) * BITS)) & ((1u << BITS) - 1u);
+  return (2u * qa) | ((2u * qa + 1u) << 8) | ((2u * qb) << 16) | ((2u * qb + 1u) << 24);
+}
+
+template <int BN, int BITS, int GS, bool IMPLIED>
+struct UqDecoder {
+  static constexpr int NC = BN / 4;
+  static constexpr int CPB = 8 / BITS;                          // codes per byte
+  static constexpr int SPB = CPB / 2;                           // selectors per byte
+  static constexpr int ND = NC * BITS >= 32 ? NC * BITS / 32 : 1;  // dwords loaded
+  static constexpr int kRawLoads = IMPLIED ? 2 : 3;
+  static constexpr int kLutWords = 256 * SPB;
+  struct Raw {
+    uint32_t d[ND];
+    uint16_t s, b;
+  };
+  rsrc_t rw, rs, rb;
+  uint32_t row_off, sb_row;
+  int h;
+
+  __device__ __forceinline__ static void init_lut(uint32_t* lut, int tid) {
+    for (int e = tid; e < kLutWords; e += kQmmThreads) lut[e] = uq_selector<BITS>((uint32_t)(e / SPB), e % SPB);
+  }
+  __device__ __forceinline__ UqDecoder(const QmmParams& p, int n, int h_) : h(h_) {
+    rw = make_rsrc(p.w, p.w_bytes);
+    rs = make_rsrc(p.s, p.sb_bytes);
+    rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
+    row_off = (uint32_t)n * (uint32_t)p.row_bytes;
+    sb_row = (uint32_t)n * (uint32_t)p.G;
+  }
+  // first code of the thread's span, within the row
+  __device__ __forceinline__ uint32_t k0(int step) const { return (uint32_t)(step * kQmmBK + NC * h); }
+  __device__ __forceinline__ void issue(int step, Raw& rw_) const {
+    // the dword holding the span's first code; rows are whole dwords
+    const uint32_t a = row_off + ((k0(step) * BITS) >> 5) * 4u;
+    if constexpr (ND == 1) {
+      rw_.d[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)a, 0, 0);
+    } else if constexpr (ND == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)a, 0, 0);
+      rw_.d[0] = v[0];
+      rw_.d[1] = v[1];
+    } else {
+      static_assert(ND == 4, "spans of 16, 32 or 64 codes");
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)a, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rw_.d[k] = v[k];
+    }
+    const uint32_t so = 2u * (sb_row + (uint32_t)((step * kQmmBK) / GS));
+    rw_.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
+    if constexpr (!IMPLIED) rw_.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, 0, 0);
+    else rw_.b = 0;
+  }
+  __device__ __forceinline__ void decode(int step, const Raw& rw_, const uint32_t* lut,
+                                         uint32_t (&out)[NC / 2]) const {
+    // the row's weights for q = 0 .. 2^BITS-1: bytes 2q, 2q+1 of {wt_hi, wt_lo}
+    const float s = h2f(__builtin_bit_cast(half_t, rw_.s));
+    const float b = IMPLIED ? -s * (BITS == 1 ? 0.5f : 1.5f) : h2f(__builtin_bit_cast(half_t, rw_.b));
+    uint32_t wt_lo, wt_hi = 0;
+    wt_lo = (uint32_t)__builtin_bit_cast(uint16_t, affine_to_half(s, 0u, b)) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, affine_to_half(s, 1u, b)) << 16);
+    if constexpr (BITS == 2)
+      wt_hi = (uint32_t)__builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b)) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, affine_to_half(s, 3u, b)) << 16);
+    // 1-bit spans of 16 codes sit in the upper half of their dword for odd h
+    uint32_t d[ND];
+#pragma unroll
+    for (int k = 0; k < ND; ++k) d[k] = rw_.d[k];
+    if constexpr (NC * BITS < 32) d[0] >>= (k0(step) * BITS) & 31u;
+    constexpr int NBYTES = NC * BITS / 8;
+#pragma unroll
+    for (int j = 0; j < NBYTES; ++j) {
+      const uint32_t v = (d[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+#pragma unroll
+      for (int e = 0; e < SPB; ++e) out[j * SPB + e] = __builtin_amdgcn_perm(wt_hi, wt_lo, lut[v * SPB + e]);
+    }
+  }
+};
+
+template <int BM, int BN, class Dec>
+__global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   constexpr int MB = BM / 32;   // 16-row MFMA blocks per wave (wave rows: BM/2)
   constexpr int NB = BN / 32;   // 16-column MFMA blocks per wave (wave columns: BN/2)
-  constexpr int NC = BN / 4;    // codes a thread decodes per step
+  constexpr int NC = Dec::NC;   // codes a thread decodes per step
   constexpr int RPW = 64 / NC;  // spans per weight row (threads per row)
+  static_assert(NC == BN / 4, "one span of BN/4 codes per producer thread");
   extern __shared__ __attribute__((aligned(16))) uint32_t qsmem[];
   half_t* xs = reinterpret_cast<half_t*>(qsmem);                  // [2][BM*64]
   half_t* ws = xs + 2 * BM * kQmmBK;                              // [2][BN*64]
-  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * BN * kQmmBK);  // [256]
+  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * BN * kQmmBK);  // [Dec::kLutWords]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,11 +331,8 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
   const int S = p.K / kQmmBK;
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
-  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
-  const rsrc_t rs = make_rsrc(p.s, p.sb_bytes);
-  const rsrc_t rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
 
-  if (tid < 256) lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
+  Dec::init_lut(lut, tid);
 
   // ---- x loads (producers): chunk c = i*4 + pw covers LDS units
   // [64c, 64c+64) of a buffer, rows 8c..8c+7; lane l loads unit 64c+l
@@ -194,51 +354,11 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
   const int pt = tid & 255;
   const int r = pt % BN, h = pt / BN;
   static_assert(RPW * BN == 256, "one span per producer thread");
-  const uint32_t row_off = (uint32_t)(n0 + r) * (uint32_t)p.row_bytes;
-  const uint32_t sb_row = (uint32_t)(n0 + r) * (uint32_t)p.G;
-  struct Raw {
-    u32x4 d;
-    uint16_t s, b;
-  };
-  auto group_base = [&](int step) { return GS == 64 ? 13 * step : 26 * (step >> 1); };
-  constexpr int P1 = GS == 128 ? 1 : 0;
-  auto span_start = [&](int step) {
-    const int par = GS == 128 ? (step & 1) : 0;
-    return par == 0 ? t5_span_start<GS, 0, NC>(h) : t5_span_start<GS, P1, NC>(h);
-  };
-  auto issue_raw = [&](int step, Raw& rw_) {
-    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
-    // 16 bytes from the dword at or below the span's first byte: a span has
-    // at most 13 bytes (14 for the second half of a 128-group, which starts
-    // 0 or 2 bytes into its dword), so the window always holds it; dwords
-    // past the end of W read as zeros
-    rw_.d = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(a & ~3u), 0, 0);
-    const uint32_t so = 2u * (sb_row + (uint32_t)((step * kQmmBK) / GS));
-    rw_.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)so, 0, 0);
-    if constexpr (!IMPLIED) rw_.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)so, 0, 0);
-    else rw_.b = 0;
-  };
-  auto decode = [&](int step, const Raw& rw_, int buf) {
-    const uint32_t a = row_off + (uint32_t)(group_base(step) + span_start(step));
-    const uint32_t sh = a & 3u;
-    uint32_t wv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(k < 3 ? rw_.d[k + 1] : 0u, rw_.d[k], sh);
-    uint64_t wt;
-    if constexpr (IMPLIED) {
-      const uint32_t sp = rw_.s, sn = rw_.s ^ 0x8000u;  // +s, -s (exact)
-      wt = (uint64_t)sn | ((uint64_t)sp << 32);
-    } else {
-      const float s = h2f(__builtin_bit_cast(half_t, rw_.s)), b = h2f(__builtin_bit_cast(half_t, rw_.b));
-      const uint32_t v0 = __builtin_bit_cast(uint16_t, affine_to_half(s, 0u, b));
-      const uint32_t v1 = __builtin_bit_cast(uint16_t, affine_to_half(s, 1u, b));
-      const uint32_t v2 = __builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b));
-      wt = (uint64_t)(v0 | (v1 << 16)) | ((uint64_t)v2 << 32);
-    }
+  const Dec dec(p, n0 + r, h);
+  typename Dec::Raw raw;
+  auto decode = [&](int step, int buf) {
     uint32_t out[NC / 2];
-    const int par = GS == 128 ? (step & 1) : 0;
-    if (par == 0) t5_decode_h<GS, 0, NC>(h, wv, wt, lut, out);
-    else t5_decode_h<GS, P1, NC>(h, wv, wt, lut, out);
+    dec.decode(step, raw, lut, out);
     half_t* wb = ws + buf * BN * kQmmBK;
 #pragma unroll
     for (int t = 0; t < NC / 8; ++t)
@@ -300,20 +420,19 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
   };
 
   // ---- prologue: step 0 in buffer 0, raw bytes of step 1 in registers
-  Raw raw;
   if (producer) {
     issue_x(0, 0);
-    issue_raw(0, raw);
+    dec.issue(0, raw);
   }
   __syncthreads();  // table built (the loads above are waited for by decode)
   if (producer) {
-    decode(0, raw, 0);
-    if (S > 1) issue_raw(1, raw);
+    decode(0, 0);
+    if (S > 1) dec.issue(1, raw);
   }
   __syncthreads();  // x of step 0 (the fence waits for the loads) and weights of step 0
 
   // loads a producer issues after a step's x loads: bytes + scale (+ bias)
-  constexpr int kRawLoads = IMPLIED ? 2 : 3;
+  constexpr int kRawLoads = Dec::kRawLoads;
   for (int st = 0; st < S; ++st) {
     const int cur = st & 1, nxt = cur ^ 1;
     if (!producer) {
@@ -321,11 +440,11 @@ __global__ __launch_bounds__(kQmmThreads) void t5_qmm_kernel(QmmParams p) {
     } else {
       if (st + 1 < S) {
         issue_x(st + 1, nxt);
-        decode(st + 1, raw, nxt);
+        decode(st + 1, nxt);
       }
       // always issued (the last steps reload the last step's bytes, unused),
       // so that the count of loads after the x loads is fixed
-      issue_raw(min(st + 2, S - 1), raw);
+      dec.issue(min(st + 2, S - 1), raw);
       // this wave's x loads of step st+1 have landed in LDS (only the loads
       // issued after them may still be in flight), its weight stores are done
       __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)

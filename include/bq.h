@@ -43,7 +43,8 @@
  * Alignment: x needs 16-byte alignment (it is read in 16-byte vectors).
  * The decode calls (qmv, qmv_wide, qmv_sym, t5_qmv, t5_qmv_wide) also read
  * scales and biases in 16-byte vectors and need them 16-byte aligned
- * (qmv_sym ignores the bias pointer); bq_t5_qmm and bq_dequant need 2 bytes.
+ * (qmv_sym ignores the bias pointer); bq_qmm, bq_t5_qmm and bq_dequant need
+ * 2 bytes.
  * y needs 2-byte alignment, except that bq_dequant with bits 1/2 writes y in
  * 16-byte vectors and needs it 16-byte aligned; w needs 4-byte alignment
  * (uint32 words for bits 1/2; dword loads for t5).  Fresh allocations from
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 4
+#define BQ_ABI_VERSION 6
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -85,12 +86,18 @@ typedef enum bq_status {
 #define BQ_LINEAR_SYM 1   /* bias implied (-scale*ratio; t5: -scale), biases never read */
 /* t5 calls of bq_linear with M >= BQ_T5_QMM_MIN_M take the fused qmm path */
 #define BQ_T5_QMM_MIN_M 17
+/* 1/2-bit calls of bq_linear take bq_qmm when M >= BQ_QMM_MIN_M and the
+ * product has at least BQ_QMM_MIN_TILES tiles of 32 x 64 outputs
+ * (ceil(N/64)*ceil(M/32)), enough to occupy half the CUs */
+#define BQ_QMM_MIN_M 17
+#define BQ_QMM_MIN_TILES 128
 
 typedef enum bq_route {
   BQ_ROUTE_QMV_WIDE = 1,  /* bits 1/2, stored bias: bq_qmv_wide per pass of <= 5 rows */
   BQ_ROUTE_QMV_SYM = 2,   /* bits 1/2, implied bias: bq_qmv_sym per pass of <= 5 rows */
   BQ_ROUTE_T5_WIDE = 3,   /* t5: bq_t5_qmv_wide per pass of <= 5 rows */
-  BQ_ROUTE_T5_QMM = 4     /* t5, M >= BQ_T5_QMM_MIN_M: one bq_t5_qmm */
+  BQ_ROUTE_T5_QMM = 4,    /* t5, M >= BQ_T5_QMM_MIN_M: one bq_t5_qmm */
+  BQ_ROUTE_QMM = 5        /* bits 1/2, M and tiles as above: one bq_qmm */
 } bq_route;
 
 /* ABI version of the loaded library; callers must refuse to use a library
@@ -138,6 +145,17 @@ int bq_t5_qmv_wide(const void* x, const void* w, const void* scales, const void*
 int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y,
               int M, int N, int K, int bits, int group_size, void* stream);
 
+/* qmm -- section 二 path 1 (1-bit prefill dequantizes to float16 and then
+ * multiplies) and path 3 (the fused unpack + matrix multiply of t5): the
+ * fused product for the uint32 formats, bits 1 or 2, any M >= 1 (prefill,
+ * M > 16 intended).  Each code word is unpacked once per weight tile;
+ * fp16 x fp16 -> fp32 on the matrix cores.  biases == NULL implies
+ * -scale*(2^bits-1)/2 and no bias is read; non-NULL biases are read.  Each
+ * weight enters the product as fp16_rne(scale*q + bias), as bq_dequant
+ * writes it. */
+int bq_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y,
+           int M, int N, int K, int bits, int group_size, void* stream);
+
 /* dequant -- section 二 path 1 (1-bit prefill dequantizes to float16
  * before a matmul): y := fp16 [N][K], y[n][k] = fp16_rne(scale*q + bias)
  * computed exactly and rounded once.  x is ignored (may be NULL) and so is
@@ -149,24 +167,26 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
 /* linear -- the routing of section 二 (the kernels are chosen by bits and
  * by the number of activation rows M) and section 三 (1/2-bit affine layers
  * in decode take the fast kernels): y = x * W^T for any M >= 1.
- *   bits 1/2: passes of up to 5 rows through bq_qmv_wide, or bq_qmv_sym when
- *             flags has BQ_LINEAR_SYM (each pass reads W once; M > 5 reads it
- *             ceil(M/5) times);
+ *   bits 1/2: one bq_qmm when M >= BQ_QMM_MIN_M and the product has
+ *             BQ_QMM_MIN_TILES tiles, else passes of up to 5 rows through
+ *             bq_qmv_wide, or bq_qmv_sym when flags has BQ_LINEAR_SYM (each
+ *             pass reads W once; M > 5 reads it ceil(M/5) times);
  *   t5:       M < BQ_T5_QMM_MIN_M: passes of up to 5 rows through
  *             bq_t5_qmv_wide; M >= BQ_T5_QMM_MIN_M: bq_t5_qmm (the
  *             article's prefill rule, M > 16).
  * Arguments as for the entry point a pass goes to; with BQ_LINEAR_SYM the
- * biases argument is ignored (may be NULL).  Results are those of the
- * entry points the passes take; each pass is validated before it launches,
- * so an invalid argument fails before anything runs.  Undefined flag bits:
- * BQ_ERR_FLAGS. */
+ * biases argument is ignored (may be NULL) and the bias is implied.
+ * Results are those of the entry points the passes take; each pass is
+ * validated before it launches, so an invalid argument fails before
+ * anything runs.  Undefined flag bits: BQ_ERR_FLAGS. */
 int bq_linear(const void* x, const void* w, const void* scales, const void* biases, void* y,
               int M, int N, int K, int bits, int group_size, int flags, void* stream);
 
-/* The route bq_linear takes for (M, bits, flags), a bq_route value, and the
- * number of kernel passes in *passes (may be NULL); BQ_ERR_M or BQ_ERR_BITS
- * for invalid arguments.  Host-only: launches nothing. */
-int bq_linear_route(int M, int bits, int flags, int* passes);
+/* The route bq_linear takes for (M, N, bits, flags), a bq_route value, and
+ * the number of kernel passes in *passes (may be NULL); BQ_ERR_M,
+ * BQ_ERR_SHAPE (N < 1) or BQ_ERR_BITS for invalid arguments.  Host-only:
+ * launches nothing. */
+int bq_linear_route(int M, int N, int bits, int flags, int* passes);
 
 /* sym detection -- section 二 path 2 (the symmetric variant applies when
  * bias = -scale * ratio holds): writes 1 to the device int *flag when every

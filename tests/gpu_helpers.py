@@ -55,6 +55,8 @@ def run_entry(entry, inp, x=None, w=None, s=None, b=None, poison_bias=False):
         y = bq.t5_qmv_wide(xd, wd, sd, gs, biases=bd)
     elif entry == "t5_qmm":
         y = bq.t5_qmm(xd, wd, sd, gs, biases=bd)
+    elif entry == "qmm":
+        y = bq.qmm(xd, wd, sd, bits, gs, biases=bd)
     else:
         raise ValueError(entry)
     torch.cuda.synchronize()

@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 4
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 6
 
 
 def test_strerror_covers_every_status(lib):
@@ -95,7 +95,7 @@ def call(lib, name, x=PX, w=PW, s=PS, b=PB, y=PY, M=1, N=8, K=256, bits=2, gs=64
     return getattr(lib, name)(x, w, s, b, y, M, N, K, bits, gs, None)
 
 
-U_ENTRIES = ["bq_qmv", "bq_qmv_wide", "bq_qmv_sym"]
+U_ENTRIES = ["bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_qmm"]
 T5_ENTRIES = ["bq_t5_qmv", "bq_t5_qmv_wide", "bq_t5_qmm"]
 
 
@@ -147,7 +147,7 @@ def test_shapes(lib, name):
     assert call(lib, name, bits=bits, K=(1 << 30) + 1024) == SHAPE
     assert call(lib, name, bits=bits, N=1, K=(1 << 26) + 1024) == SHAPE
     assert call(lib, name, bits=bits, N=8192, K=1 << 20) == SHAPE  # packed rows past 2^30 bytes
-    if name not in ("bq_t5_qmm", "bq_dequant"):
+    if name not in ("bq_t5_qmm", "bq_qmm", "bq_dequant"):
         # a workgroup's scale rows no longer fit LDS
         assert call(lib, name, bits=bits, N=2, K=4093 * 64 + (192 if name in T5_ENTRIES else 0)) == SHAPE
 
@@ -182,6 +182,7 @@ def test_t5_needs_k_multiple_of_256(lib):
 
 def test_qmm_and_dequant_vector_alignment(lib):
     assert call(lib, "bq_t5_qmm", bits=0, x=PX + 8) == ALIGN
+    assert call(lib, "bq_qmm", bits=1, x=PX + 8) == ALIGN
     assert call(lib, "bq_dequant", bits=2, y=PY + 8) == ALIGN
 
 
@@ -211,31 +212,42 @@ def test_binding_tensor_helpers_refuse_cpu_tensors():
 
 # ---------------------------------------------------------------- dispatcher
 def test_linear_routes():
+    gate, down = 17408, 5120
     # bits 1/2: passes of up to five rows through the wide or symmetric kernel
     for bits in (1, 2):
         for M in (1, 2, 5):
-            assert bq.bq_linear_route(M, bits) == ("qmv_wide", 1)
-            assert bq.bq_linear_route(M, bits, bq.LINEAR_SYM) == ("qmv_sym", 1)
-        assert bq.bq_linear_route(6, bits) == ("qmv_wide", 2)
-        assert bq.bq_linear_route(16, bits) == ("qmv_wide", 4)
-        assert bq.bq_linear_route(17, bits, bq.LINEAR_SYM) == ("qmv_sym", 4)
-        assert bq.bq_linear_route(2048, bits) == ("qmv_wide", 410)
+            assert bq.bq_linear_route(M, gate, bits) == ("qmv_wide", 1)
+            assert bq.bq_linear_route(M, gate, bits, bq.LINEAR_SYM) == ("qmv_sym", 1)
+        assert bq.bq_linear_route(6, gate, bits) == ("qmv_wide", 2)
+        assert bq.bq_linear_route(16, gate, bits) == ("qmv_wide", 4)
+        # the fused product from 17 rows when there are 128 tiles of 32 x 64
+        assert bq.QMM_MIN_M == 17 and bq.QMM_MIN_TILES == 128
+        assert bq.bq_linear_route(17, gate, bits) == ("qmm", 1)
+        assert bq.bq_linear_route(17, gate, bits, bq.LINEAR_SYM) == ("qmm", 1)
+        assert bq.bq_linear_route(17, down, bits) == ("qmv_wide", 4)      # 80 tiles
+        assert bq.bq_linear_route(32, down, bits) == ("qmv_wide", 7)
+        assert bq.bq_linear_route(33, down, bits) == ("qmm", 1)           # 160 tiles
+        assert bq.bq_linear_route(17, 64 * 128, bits) == ("qmm", 1)
+        assert bq.bq_linear_route(17, 64 * 127, bits) == ("qmv_wide", 4)
+        assert bq.bq_linear_route(2048, down, bits) == ("qmm", 1)
     # t5: wide passes below 17 rows, the fused product from 17 (M > 16)
     assert bq.T5_QMM_MIN_M == 17
     for M in (1, 5):
-        assert bq.bq_linear_route(M, bq.BITS_T5) == ("t5_qmv_wide", 1)
-        assert bq.bq_linear_route(M, bq.BITS_T5, bq.LINEAR_SYM) == ("t5_qmv_wide", 1)
-    assert bq.bq_linear_route(16, bq.BITS_T5) == ("t5_qmv_wide", 4)
-    assert bq.bq_linear_route(17, bq.BITS_T5) == ("t5_qmm", 1)
-    assert bq.bq_linear_route(512, bq.BITS_T5) == ("t5_qmm", 1)
+        assert bq.bq_linear_route(M, gate, bq.BITS_T5) == ("t5_qmv_wide", 1)
+        assert bq.bq_linear_route(M, gate, bq.BITS_T5, bq.LINEAR_SYM) == ("t5_qmv_wide", 1)
+    assert bq.bq_linear_route(16, gate, bq.BITS_T5) == ("t5_qmv_wide", 4)
+    assert bq.bq_linear_route(17, gate, bq.BITS_T5) == ("t5_qmm", 1)
+    assert bq.bq_linear_route(17, 64, bq.BITS_T5) == ("t5_qmm", 1)
+    assert bq.bq_linear_route(512, gate, bq.BITS_T5) == ("t5_qmm", 1)
 
 
 def test_linear_route_errors(lib):
-    assert lib.bq_linear_route(0, 2, 0, None) == MRANGE
-    assert lib.bq_linear_route(-4, 2, 0, None) == MRANGE
-    assert lib.bq_linear_route(1, 3, 0, None) == BITS
+    assert lib.bq_linear_route(0, 8, 2, 0, None) == MRANGE
+    assert lib.bq_linear_route(-4, 8, 2, 0, None) == MRANGE
+    assert lib.bq_linear_route(1, 0, 2, 0, None) == SHAPE
+    assert lib.bq_linear_route(1, 8, 3, 0, None) == BITS
     with pytest.raises(bq.BQError):
-        bq.bq_linear_route(0, 2)
+        bq.bq_linear_route(0, 8, 2)
 
 
 FLAGS = -8
@@ -260,6 +272,10 @@ def test_linear_validates_before_launch(lib):
     assert lcall(lib, bits=0, K=192, b=None) == ALIGN
     assert lcall(lib, bits=0, M=17, K=192, b=None) == ALIGN
     assert lcall(lib, bits=0, M=17, w=None, b=None) == NULL
+    # the 1/2-bit fused route validates too, and needs stored biases without the sym flag
+    assert lcall(lib, M=17, N=8192, b=None) == NULL
+    assert lcall(lib, M=17, N=8192, x=PX + 8) == ALIGN
+    assert lcall(lib, M=17, N=8192, flags=1, y=PY + 1) == ALIGN
 
 
 def test_sym_check_validates(lib):

@@ -120,7 +120,7 @@ def test_linear_t5_routes(gs, M):
     y = to_np(bq.linear(x, qw))
     torch.cuda.synchronize()
     assert_close(y.astype(np.float64), inp, what=f"linear t5 gs{gs} M{M}")
-    route, passes = bq.bq_linear_route(M, bq.BITS_T5)
+    route, passes = bq.bq_linear_route(M, N, bq.BITS_T5)
     if route == "t5_qmm":
         ref = to_np(bq.t5_qmm(x, qw.w, qw.scales, gs))
         assert np.array_equal(y.view(np.uint16), ref.view(np.uint16))
@@ -142,3 +142,27 @@ def test_linear_t5_stored_bias_and_sym_flag():
     ys = to_np(bq.linear(dev(inp.x), qw, sym=True))
     yn = to_np(bq.linear(dev(inp.x), _qw(bq, inp, biases=None)))
     assert np.array_equal(ys.view(np.uint16), yn.view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt,gs", [("u2", 64), ("u1", 128)])
+@pytest.mark.parametrize("M,NN", [(17, 8192), (16, 8192), (40, 5120), (64, 17408)])
+def test_linear_1_2_bit_prefill_routes(fmt, gs, M, NN):
+    """From 17 rows with enough tiles bq_linear takes the fused product and
+    gives its bits; otherwise five-row wide passes."""
+    bq, torch = _bq()
+    inp = make(fmt, M, NN, 1024, gs, "asym", seed=101)
+    bits = 1 if fmt == "u1" else 2
+    qw = _qw(bq, inp)
+    qw._sym = False  # the affine route (the random biases are not symmetric)
+    x = dev(inp.x)
+    y = to_np(bq.linear(x, qw))
+    torch.cuda.synchronize()
+    assert_close(y.astype(np.float64), inp, rows=None if NN <= 2048 else np.arange(0, NN, 97),
+                 what=f"linear {fmt} M{M} N{NN}")
+    route, passes = bq.bq_linear_route(M, NN, bits)
+    if route == "qmm":
+        ref = to_np(bq.qmm(x, qw.w, qw.scales, bits, gs, biases=qw.biases))
+    else:
+        ref = np.concatenate([to_np(bq.qmv_wide(x[m0:m0 + 5].contiguous(), qw.w, qw.scales, qw.biases, bits, gs))
+                              for m0 in range(0, M, 5)])
+    assert np.array_equal(y.view(np.uint16), ref.view(np.uint16)), route
