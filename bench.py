@@ -201,12 +201,18 @@ def cpu_baseline(shapes):
 
 
 def kernel_source_hash():
+    """Hash of the decode kernel's own sources: qmv_kernels.hpp and the
+    qmv-family launch section of bq_api.hip (geometry and launch
+    configuration).  Counter results are tied to it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_decode_qmv_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+    with open(os.path.join(csrc, "qmv_kernels.hpp"), "rb") as f:
+        h.update(f.read())
+    with open(os.path.join(csrc, "bq_api.hip"), "r", encoding="utf-8") as f:
+        api = f.read()
+    start = api.index("// ---------------------------------------------------------------- qmv family")
+    end = api.index("// ---------------------------------------------------------------- qmm")
+    h.update(api[start:end].encode())
     return h.hexdigest()[:16]
 
 
@@ -250,16 +256,19 @@ def full_suite(torch, lib, dev, path):
         for shape in ("gate", "down"):
             N, K = synth.PROJECTION_SHAPES[shape]
             qmm_specs.append(("bq_t5_qmm", "t5", M, N, K, 128, "t5", shape))
+            for fmt in ("u1", "u2"):
+                qmm_specs.append(("bq_qmm", fmt, M, N, K, 128, "asym", shape))
     with open(path, "w") as f:
         f.write("entry,fmt,variant,M,shape,N,K,gs,us,GBps,frac_hbm,TFLOPs\n")
         for spec in specs + qmm_specs:
             copies = make_calls(torch, dev, [spec])
             pair = [cs[0] for cs in copies]
-            launches = 8 if spec[0] == "bq_t5_qmm" and spec[2] >= 512 else 40
+            mm = spec[0] in ("bq_t5_qmm", "bq_qmm")
+            launches = 8 if mm and spec[2] >= 512 else 40
             t = per_call_seconds(torch, lib, pair, launches=launches, replays=3)
             c = pair[0]
             gbs = c.bytes / t / 1e9
-            tflops = (2.0 * c.M * c.N * c.K / t / 1e12) if spec[0] == "bq_t5_qmm" else 0.0
+            tflops = (2.0 * c.M * c.N * c.K / t / 1e12) if mm else 0.0
             line = (f"{spec[0]},{spec[1]},{spec[6]},{spec[2]},{spec[7]},{spec[3]},{spec[4]},{spec[5]},"
                     f"{t * 1e6:.3f},{gbs:.1f},{gbs / PEAK_HBM_GBS:.4f},{tflops:.1f}")
             f.write(line + "\n")
@@ -268,7 +277,65 @@ def full_suite(torch, lib, dev, path):
             rows.append(line)
             del copies, pair
             torch.cuda.empty_cache()
+        for line in spec_and_repack_rows(torch, lib, dev):
+            f.write(line + "\n")
+            f.flush()
+            print(line, file=sys.stderr, flush=True)
+            rows.append(line)
     return rows
+
+
+def spec_and_repack_rows(torch, lib, dev):
+    """Timing of bq_spec_decode_verify (Qwen vocabulary, fp16 logits) and of
+    bq_t5_repack (2-bit gate weights), as CSV rows; GB/s of the bytes each
+    call must read and write."""
+    import ctypes
+
+    import numpy as np
+    import synth
+    out = []
+    stream = torch.cuda.current_stream().cuda_stream
+    for B, L in ((1, 4), (8, 4), (8, 7)):
+        V = synth.QWEN_VOCAB
+        s = synth.make_spec_inputs(B, L, V, dtype=np.float16, seed=0)
+        lg = upload(torch, s.logits, dev)
+        dr = upload(torch, s.draft, dev)
+        n = ctypes.c_size_t(0)
+        lib.bq_spec_verify_workspace(B, L, V, ctypes.byref(n))
+        ws = torch.zeros(n.value, dtype=torch.uint8, device=dev)
+        a = torch.empty(B, dtype=torch.int32, device=dev)
+        nx = torch.empty(B, dtype=torch.int32, device=dev)
+
+        def one():
+            st = lib.bq_spec_decode_verify(lg.data_ptr(), 1, dr.data_ptr(), B, L, V, a.data_ptr(), nx.data_ptr(),
+                                           None, ws.data_ptr(), n.value, stream)
+            if st != 0:
+                raise RuntimeError(f"bq_spec_decode_verify: status {st}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                one()
+        g.replay()
+        t = time_graphs(torch, [g], 5) / 100
+        nbytes = B * (L + 1) * V * 2
+        gbs = nbytes / t / 1e9
+        out.append(f"bq_spec_decode_verify,f16,B{B},{L},vocab,{B * (L + 1)},{V},0,{t * 1e6:.3f},{gbs:.1f},"
+                   f"{gbs / PEAK_HBM_GBS:.4f},0.0")
+    N, K = synth.PROJECTION_SHAPES["gate"]
+    inp = synth.make_inputs("u2", 1, N, K, 128, "asym", seed=0)
+    w = upload(torch, inp.w, dev)
+    o = torch.empty((N, (K // 128) * 26), dtype=torch.uint8, device=dev)
+    flag = torch.empty(1, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            lib.bq_t5_repack(w.data_ptr(), o.data_ptr(), N, K, 2, 128, flag.data_ptr(), stream)
+    g.replay()
+    t = time_graphs(torch, [g], 3) / 30
+    nbytes = w.numel() * 4 + o.numel()
+    gbs = nbytes / t / 1e9
+    out.append(f"bq_t5_repack,u2,asym,0,gate,{N},{K},128,{t * 1e6:.3f},{gbs:.1f},{gbs / PEAK_HBM_GBS:.4f},0.0")
+    return out
 
 
 def counter_run(torch, lib, dev):
