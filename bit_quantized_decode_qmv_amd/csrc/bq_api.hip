@@ -143,14 +143,23 @@ int launch_qmv_p(const QmvParams& p, void* stream) {
 }
 
 // Rows per unit R and units in flight per slot P never change a row's
-// arithmetic.  R = 4 halves the per-code share of the per-unit work; it is
-// used for one or two activation rows, where the registers allow it, and
-// where a 4-row workgroup's scale rows fit one staging pass.  A shallow ring
-// is faster: with every slot of the GPU asking for many units at once, HBM
-// returns them in no useful order and each slot waits for its oldest one,
-// and every fetch past a slot's last unit still costs issue slots.
+// arithmetic.  R = 4 quarters the per-code share of the per-unit work
+// (cross-lane sums, scale reads, cursor arithmetic); it is used wherever the
+// registers allow it and a 4-row workgroup's scale rows fit one staging
+// pass.  Small products (k and v of the decoder, N = 1024) leave most slots
+// without a 4-row unit, so one slot's unit is the whole critical path; when
+// 1-row units give every slot at most one unit they are used instead (about
+// 4x as many slots share the arithmetic).  A shallow ring is faster: with
+// every slot of the GPU asking for many units at once, the x and scale
+// loads queue behind the weights and the staging barrier comes later, while
+// the loop cannot get shorter than its arithmetic.
 template <int FMT, int GS, int M, bool IMPLIED>
 int launch_qmv_t(QmvParams p, void* stream) {
+  {
+    QmvParams p1 = p;
+    if (qmv_geometry(p1, M, 1) && units_per_slot(p1, 1) <= 1)
+      return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 1>(p1, stream);
+  }
   if (qmv_geometry(p, M, 4)) {
     if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
     return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);

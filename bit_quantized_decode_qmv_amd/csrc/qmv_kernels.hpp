@@ -11,17 +11,18 @@
 // gfx950 design
 // -------------
 // * One workgroup of 8 waves per CU.  A wave holds four slots of 16 lanes;
-//   the 16 lanes of a slot cover one 1024-code K tile of R = 2 rows, each
+//   the 16 lanes of a slot cover one 1024-code K tile of R = 1, 2 or 4 rows, each
 //   lane one chunk: 64 codes of 1/2-bit words (8 or 16 bytes) or one
 //   13-byte t5 run (a whole 64-group, or half of a 128-group: 65 + 63 codes).
-// * Work unit = (row-group of R rows, K tile).  The units of a workgroup,
-//   row-major, are cut into one contiguous range per slot; a slot keeps a
-//   ring of P units in flight, so HBM reads overlap the arithmetic without
-//   any barrier.  Consecutive units of one row-group accumulate in
-//   registers; each run is reduced over the slot's lanes into LDS, keyed by
-//   its first unit, and at the end every row adds its runs in unit order.
-//   The decomposition depends on N, K and the format only -- never on M --
-//   so row m of a wide call is bit-identical to a call with that row alone.
+// * Work unit = (row-group of R rows, K tile).  A workgroup's units, in the
+//   order of their bytes, are dealt to its slots cyclically (slot k: units
+//   k, k + 32, ...), so at every step its slots read one contiguous stretch
+//   of its rows; a slot keeps a ring of P units in flight, so HBM reads
+//   overlap the arithmetic without any barrier.  Each unit's partial sums
+//   are reduced over the slot's lanes into LDS, keyed by (row-group, tile),
+//   and at the end every row adds its tiles in order.  Nothing in a row's
+//   sums depends on M, R, P or the slot that took a unit, so row m of a
+//   wide call is bit-identical to a call with that row alone.
 // * x is staged per segment of K tiles in LDS, permuted into the order in
 //   which the unpack below produces code pairs and pre-scaled per code
 //   position.  Its loads are issued before the ring loads so that waiting
@@ -59,7 +60,7 @@ constexpr int kKL = 16;            // lanes per slot (chunks per tile)
 constexpr int kWaves = 8;          // waves per workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = kThreads / kKL;
-constexpr int kR = 2;              // rows per row-group, at least (the kernels take R = 2 or 4)
+constexpr int kR = 2;              // rows per row-group of the scale-staging limit (the kernels take R = 1, 2 or 4)
 constexpr int kXD = 36;            // LDS dwords per staged chunk (32-35 used)
 
 struct QmvParams {
