@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="q,k,v,o,down",
+    ap.add_argument("--cpu-sample", default="q,k,v,o,gate,up,down",
                     help="shapes (2-bit, gs=64, M=1) timed with the CPU oracle")
     ap.add_argument("--suite", default="", help="'full': also time M=1..5 wide/sym, t5 and qmm "
                     "configurations and write them to --detail-csv")
