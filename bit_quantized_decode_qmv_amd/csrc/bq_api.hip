@@ -235,16 +235,46 @@ template <int BN, int BITS, int GS, bool IMPLIED>
 using QmmDecoder = typename std::conditional<BITS == BQ_BITS_T5, T5Decoder<BN, GS, IMPLIED>,
                                              UqDecoder<BN, (BITS == 1 ? 1 : 2), GS, IMPLIED>>::type;
 
-template <int BM, int BN, int BITS, int GS, bool IMPLIED>
-int launch_qmm_t(const QmmParams& p, void* stream) {
+template <int BM, int BN, int BITS, int GS, bool IMPLIED, int SUB>
+int launch_qmm_s(const QmmParams& p, void* stream) {
   typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
-  const void* fn = reinterpret_cast<const void*>(&qmm_kernel<BM, BN, Dec>);
-  const size_t lds = qmm_lds_bytes(BM, BN, Dec::kLutWords);
+  const void* fn = reinterpret_cast<const void*>(&qmm_kernel<BM, BN, Dec, SUB>);
+  const size_t lds = qmm_lds_bytes(BM, BN, Dec::kLutWords, SUB);
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
   dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   QmmParams q = p;
   return launch(fn, grid, dim3(kQmmThreads), lds, stream, &q);
+}
+
+// K steps per pipeline iteration of a tile shape: the small tiles (whose
+// 64-code step is much shorter than a memory round trip) take 4 (32 x 64,
+// 64 x 64) or 2 (32 x 128), as far as the LDS of one workgroup per CU and
+// the step count K/64 allow; the others 1.
+constexpr int qmm_sub(int BM, int BN) { return (BM <= 64 && BN == 64) ? 4 : (BM == 32 && BN == 128) ? 2 : 1; }
+
+// sub: the K steps per iteration wanted (4, 2 or 1); reduced to what the
+// tile's LDS allows (qmm_sub) and what divides the step count
+template <int BM, int BN, int BITS, int GS, bool IMPLIED>
+int launch_qmm_t(const QmmParams& p, int sub, void* stream) {
+  constexpr int SUB = qmm_sub(BM, BN);
+  const int steps = p.K / kQmmBK;
+  if (sub >= 4 && SUB >= 4 && steps % 4 == 0) return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, (SUB >= 4 ? 4 : 1)>(p, stream);
+  if (sub >= 2 && SUB >= 2 && steps % 2 == 0) return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, (SUB >= 2 ? 2 : 1)>(p, stream);
+  return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, 1>(p, stream);
+}
+
+// Small products (M <= 32, only 32-row tiles) are bound by the time of one
+// pipeline iteration, not by the MFMA or memory throughput: measured on
+// MI355X at M = 32, an iteration of SUB steps takes about 0.57 us plus
+// 0.43 us per step with 64-column tiles and 0.50 us per step with 128-column
+// tiles.  Estimated microseconds of (BN, SUB) over `tiles` workgroups (two
+// per CU only for 32 x 64 tiles without SUB, whose LDS allows it).
+double qmm_small_m_us(int tiles, int steps, int BN, int sub) {
+  const int per_cu = (BN == 64 && sub == 1) ? 2 : 1;
+  const double rounds = std::ceil((double)tiles / (256.0 * per_cu));
+  const double iter = 0.57 + sub * (BN == 64 ? 0.43 : 0.50);
+  return rounds * ((double)steps / sub) * iter;
 }
 
 // Estimated cycles of one call with BM x BN tiles: per K step the larger of
@@ -273,7 +303,7 @@ double qmm_cost(int M, int N, int K, int BM, int BN, int lut_words, double alu_p
 
 template <int BITS, int GS, bool IMPLIED>
 int launch_qmm_m(const QmmParams& p, void* stream) {
-  typedef int (*Fn)(const QmmParams&, void*);
+  typedef int (*Fn)(const QmmParams&, int, void*);
   struct Cand {
     int bm, bn;
     Fn fn;
@@ -290,6 +320,24 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
   const int lut_words = QmmDecoder<64, BITS, GS, IMPLIED>::kLutWords;
   const double alu = BITS == BQ_BITS_T5 ? 2.5 : 1.5;
   const double wbytes = BITS == BQ_BITS_T5 ? 0.2 : BITS / 8.0;
+  const int steps = p.K / kQmmBK;
+  if (p.M <= 32) {
+    // 32 x 64 (SUB 1 or 4) or 32 x 128 (SUB 1 or 2), whichever the measured
+    // iteration times say is shortest
+    const int t64 = (p.N + 63) / 64, t128 = (p.N + 127) / 128;
+    struct Opt {
+      int bn, sub;
+      double us;
+    } opts[] = {{64, 1, qmm_small_m_us(t64, steps, 64, 1)},
+                {64, 4, steps % 4 == 0 ? qmm_small_m_us(t64, steps, 64, 4) : 1e30},
+                {128, 1, qmm_small_m_us(t128, steps, 128, 1)},
+                {128, 2, steps % 2 == 0 ? qmm_small_m_us(t128, steps, 128, 2) : 1e30}};
+    const Opt* o = &opts[0];
+    for (const Opt& c : opts)
+      if (c.us < o->us) o = &c;
+    return o->bn == 64 ? launch_qmm_t<32, 64, BITS, GS, IMPLIED>(p, o->sub, stream)
+                       : launch_qmm_t<32, 128, BITS, GS, IMPLIED>(p, o->sub, stream);
+  }
   const Cand* best = nullptr;
   double best_cost = 0.0;
   for (const Cand& c : cands) {
@@ -300,7 +348,11 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
       best_cost = cost;
     }
   }
-  return best->fn(p, stream);
+  // the 64 x 64 tile iterates over SUB = 4 steps when all its workgroups run
+  // at once (one per CU: its LDS then holds no second workgroup)
+  const int tiles = ((p.N + best->bn - 1) / best->bn) * ((p.M + best->bm - 1) / best->bm);
+  const int sub = (best->bm == 64 && best->bn == 64 && tiles <= 256) ? 4 : 1;
+  return best->fn(p, sub, stream);
 }
 
 template <int BITS>

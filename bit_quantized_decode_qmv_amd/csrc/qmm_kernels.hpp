@@ -57,8 +57,8 @@ struct QmmParams {
 constexpr int kQmmBK = 64;        // codes per K step
 constexpr int kQmmThreads = 512;  // 4 MFMA waves (2 x 2 over the tile) + 4 loading/decoding waves
 
-constexpr size_t qmm_lds_bytes(int BM, int BN, int lut_words) {
-  return (size_t)2 * BM * kQmmBK * 2 + (size_t)2 * BN * kQmmBK * 2 + (size_t)lut_words * 4;
+constexpr size_t qmm_lds_bytes(int BM, int BN, int lut_words, int SUB = 1) {
+  return (size_t)2 * SUB * BM * kQmmBK * 2 + (size_t)2 * SUB * BN * kQmmBK * 2 + (size_t)lut_words * 4;
 }
 
 // 16-byte unit (row, q) of a 128-byte LDS row
@@ -304,7 +304,13 @@ struct UqDecoder {
   }
 };
 
-template <int BM, int BN, class Dec>
+// SUB: K steps per pipeline iteration.  Each iteration's x and weight bytes
+// are requested one iteration ahead and waited for at its end, so one
+// iteration costs at least a memory round trip (about a microsecond); with
+// small tiles a single 64-code step is much shorter than that, and SUB
+// steps per iteration divide that floor by SUB.  The products and their
+// order are the same for every SUB.
+template <int BM, int BN, class Dec, int SUB>
 __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   constexpr int MB = BM / 32;   // 16-row MFMA blocks per wave (wave rows: BM/2)
   constexpr int NB = BN / 32;   // 16-column MFMA blocks per wave (wave columns: BN/2)
@@ -312,9 +318,9 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   constexpr int RPW = 64 / NC;  // spans per weight row (threads per row)
   static_assert(NC == BN / 4, "one span of BN/4 codes per producer thread");
   extern __shared__ __attribute__((aligned(16))) uint32_t qsmem[];
-  half_t* xs = reinterpret_cast<half_t*>(qsmem);                  // [2][BM*64]
-  half_t* ws = xs + 2 * BM * kQmmBK;                              // [2][BN*64]
-  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * BN * kQmmBK);  // [Dec::kLutWords]
+  half_t* xs = reinterpret_cast<half_t*>(qsmem);                        // [2][SUB][BM*64]
+  half_t* ws = xs + 2 * SUB * BM * kQmmBK;                              // [2][SUB][BN*64]
+  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * SUB * BN * kQmmBK);  // [Dec::kLutWords]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,7 +334,8 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   const int t = (int)blockIdx.x;
   const int m0 = (t / tiles_n) * BM;
   const int n0 = (t % tiles_n) * BN;
-  const int S = p.K / kQmmBK;
+  const int S = p.K / kQmmBK;  // K steps, a multiple of SUB
+  const int IT = S / SUB;      // pipeline iterations
 
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
 
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
 
   // ---- x loads (producers): chunk c = i*4 + pw covers LDS units
   // [64c, 64c+64) of a buffer, rows 8c..8c+7; lane l loads unit 64c+l
-  auto issue_x = [&](int step, int buf) {
+  auto issue_x = [&](int step, int buf) {  // buf: buffer slot (iteration buffer * SUB + sub-step)
     const int k0 = step * kQmmBK;
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) {
@@ -355,10 +362,10 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   const int r = pt % BN, h = pt / BN;
   static_assert(RPW * BN == 256, "one span per producer thread");
   const Dec dec(p, n0 + r, h);
-  typename Dec::Raw raw;
-  auto decode = [&](int step, int buf) {
+  typename Dec::Raw raw[SUB];
+  auto decode = [&](int step, int buf, int u) {  // raw bytes of sub-step u into buffer slot buf
     uint32_t out[NC / 2];
-    dec.decode(step, raw, lut, out);
+    dec.decode(step, raw[u], lut, out);
     half_t* wb = ws + buf * BN * kQmmBK;
 #pragma unroll
     for (int t = 0; t < NC / 8; ++t)
@@ -384,8 +391,10 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   constexpr int KS = kQmmBK / 32;
   constexpr int KG = (MB + NB) <= 6 ? KS : 1;  // 32-code halves per group
   auto multiply = [&](int buf) {
-    const half_t* xb = xs + buf * BM * kQmmBK;
-    const half_t* wb = ws + buf * BN * kQmmBK;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+    const half_t* xb = xs + (buf * SUB + u) * BM * kQmmBK;
+    const half_t* wb = ws + (buf * SUB + u) * BN * kQmmBK;
 #pragma unroll
     for (int g = 0; g < KS; g += KG) {
       half8_t af[KG][MB], bf[KG][NB];
@@ -417,39 +426,53 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
       asm volatile("" ::"s"(done) : "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
+    }
   };
 
-  // ---- prologue: step 0 in buffer 0, raw bytes of step 1 in registers
+  // ---- prologue: iteration 0 (steps 0 .. SUB-1) in buffer 0, raw bytes of
+  // iteration 1 in registers
   if (producer) {
-    issue_x(0, 0);
-    dec.issue(0, raw);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) issue_x(u, u);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) dec.issue(u, raw[u]);
   }
   __syncthreads();  // table built (the loads above are waited for by decode)
   if (producer) {
-    decode(0, 0);
-    if (S > 1) dec.issue(1, raw);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) decode(u, u, u);
+    if (IT > 1) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) dec.issue(SUB + u, raw[u]);
+    }
   }
-  __syncthreads();  // x of step 0 (the fence waits for the loads) and weights of step 0
+  __syncthreads();  // x of iteration 0 (the fence waits for the loads) and its weights
 
-  // loads a producer issues after a step's x loads: bytes + scale (+ bias)
-  constexpr int kRawLoads = Dec::kRawLoads;
-  for (int st = 0; st < S; ++st) {
-    const int cur = st & 1, nxt = cur ^ 1;
+  // loads a producer issues after an iteration's x loads: bytes + scale
+  // (+ bias) of each of the SUB steps of the iteration after
+  constexpr int kRawLoads = Dec::kRawLoads * SUB;
+  static_assert(kRawLoads <= 15, "vmcnt field");
+  for (int it = 0; it < IT; ++it) {
+    const int cur = it & 1, nxt = cur ^ 1;
     if (!producer) {
       multiply(cur);
     } else {
-      if (st + 1 < S) {
-        issue_x(st + 1, nxt);
-        decode(st + 1, nxt);
+      if (it + 1 < IT) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) issue_x((it + 1) * SUB + u, nxt * SUB + u);
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) decode((it + 1) * SUB + u, nxt * SUB + u, u);
       }
-      // always issued (the last steps reload the last step's bytes, unused),
-      // so that the count of loads after the x loads is fixed
-      dec.issue(min(st + 2, S - 1), raw);
-      // this wave's x loads of step st+1 have landed in LDS (only the loads
-      // issued after them may still be in flight), its weight stores are done
+      // always issued (the last iterations reload the last step's bytes,
+      // unused), so that the count of loads after the x loads is fixed
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) dec.issue(min((it + 2) * SUB + u, S - 1), raw[u]);
+      // this wave's x loads of iteration it+1 have landed in LDS (only the
+      // loads issued after them may still be in flight), its weight stores
+      // are done
       __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)
     }
-    // every wave is past step st: buffer cur is free, buffer nxt is full
+    // every wave is past iteration it: buffer cur is free, buffer nxt is full
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }

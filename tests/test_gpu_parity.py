@@ -283,7 +283,11 @@ def test_t5_qmm_tile_shapes_explicit_bias():
 # for bit, with enough tiles that two workgroups share a CU (512 and more).
 @pytest.mark.parametrize("M,N,K,gs,variant", [(20, 65536, 256, 64, "t5"), (20, 65536, 256, 128, "t5"),
                                               (100, 65536, 256, 64, "t5"), (32, 65536, 512, 64, "asym"),
-                                              (300, 16384, 512, 128, "t5"), (600, 17408, 768, 64, "t5")])
+                                              (300, 16384, 512, 128, "t5"), (600, 17408, 768, 64, "t5"),
+                                              # several K steps per pipeline iteration: 32 x 64 tiles
+                                              # (4 steps), 64 x 64 tiles in one round (4 steps)
+                                              (32, 1024, 1024, 128, "t5"), (24, 2048, 512, 64, "asym"),
+                                              (64, 4096, 768, 64, "t5"), (48, 2048, 1024, 128, "asym")])
 def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
     import bit_quantized_decode_qmv_amd as bq
     inp = make("t5", M, N, K, gs, variant, seed=31)

@@ -44,7 +44,10 @@ def test_qmm_parity(fmt, variant, gs, M, N, K):
 # one-hot activation rows read every weight back exactly (one product each)
 @pytest.mark.parametrize("fmt,gs,variant,M,N,K", [("u2", 64, "asym", 20, 65536, 256), ("u1", 128, "sym", 20, 65536, 256),
                                                   ("u2", 128, "sym", 100, 65536, 256), ("u1", 64, "asym", 32, 65536, 512),
-                                                  ("u2", 64, "sym", 300, 16384, 512)])
+                                                  ("u2", 64, "sym", 300, 16384, 512),
+                                                  # several K steps per pipeline iteration (32 x 64, 64 x 64)
+                                                  ("u2", 128, "asym", 32, 1024, 1024), ("u1", 64, "sym", 24, 2048, 512),
+                                                  ("u2", 64, "asym", 64, 4096, 768), ("u1", 128, "asym", 48, 2048, 1024)])
 def test_qmm_one_hot_rows_read_exact_weights(fmt, gs, variant, M, N, K):
     import bit_quantized_decode_qmv_amd as bq
     inp = make(fmt, M, N, K, gs, variant, seed=92)
