@@ -64,15 +64,27 @@ constexpr size_t qmm_lds_bytes(int BM, int BN, int lut_words, int SUB = 1) {
 // 16-byte unit (row, q) of a 128-byte LDS row
 __device__ __forceinline__ int qmm_swz(int row, int q) { return row * 8 + (q ^ (row & 7)); }
 
-// Digit table entry: digit i of byte v, times 16, in bits 6i..6i+5.
-__device__ __forceinline__ uint32_t t5_shift_fields(uint32_t v) {
-  uint32_t f = 0;
+// v_perm_b32 selector of a code pair (a, b): bytes 2a, 2a+1 and 2b, 2b+1 of
+// the row's weight table {w0, w1 | w2} (two fp16 weights per dword), which
+// places the fp16 weights of codes a and b in the low and high half.
+__device__ __forceinline__ uint32_t t5_pair_sel(uint32_t a, uint32_t b) {
+  return (2u * a) | ((2u * a + 1u) << 8) | ((2u * b) << 16) | ((2u * b + 1u) << 24);
+}
+
+// Pair table entry k (0..3) of byte v: the selectors of its digit pairs
+// (d0, d1), (d2, d3), (d1, d2), (d3, d4); a pair that starts on digit 4
+// takes the high half of entry 3 and the low half of the next byte's
+// entry 0.  Bytes above 242 are invalid and get 0.
+__device__ __forceinline__ uint32_t t5_pair_entry(uint32_t v, int k) {
+  if (v >= 243u) return 0u;
+  uint32_t d[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    f |= ((v % 3u) * 16u) << (6 * i);
+    d[i] = v % 3u;
     v /= 3u;
   }
-  return f;
+  const int a = k == 0 ? 0 : k == 1 ? 2 : k == 2 ? 1 : 3;
+  return t5_pair_sel(d[a], d[a + 1]);
 }
 
 // Where code c (0..GS-1) of a group sits in the group's bytes: 64-groups
@@ -89,30 +101,35 @@ template <int GS, int PAR, int H, int NC> struct T5Span {
 };
 
 // Decodes the thread's NC codes: wv = the 16 bytes from the span's first
-// byte, wt = the row's three fp16 weights (bits 0-15: q = 0, 16-31: q = 1,
-// 32-47: q = 2), lut = digit table.  Out: NC/2 dwords, code pairs (2t, 2t+1)
-// in dword t.
+// byte, wt_lo/wt_hi = the row's three fp16 weights (wt_lo: q = 0 low half,
+// q = 1 high half; wt_hi: q = 2 low half), lut = pair table.  Out: NC/2
+// dwords, code pairs (2t, 2t+1) in dword t.  Each pair costs one v_perm_b32
+// (plus one v_alignbit_b32 where the pair spans two bytes).
 template <int GS, int PAR, int H, int NC>
-__device__ __forceinline__ void t5_decode(const uint32_t (&wv)[4], uint64_t wt, const uint32_t* lut,
-                                          uint32_t (&out)[NC / 2]) {
+__device__ __forceinline__ void t5_decode(const uint32_t (&wv)[4], uint32_t wt_lo, uint32_t wt_hi,
+                                          const uint32_t* lut, uint32_t (&out)[NC / 2]) {
   using S = T5Span<GS, PAR, H, NC>;
   constexpr int nb = t5_byte_of<GS>(S::c0 + NC - 1) - S::start + 1;  // bytes used
   static_assert(nb <= 14, "span of at most 14 bytes");
-  uint32_t f[14];
+  u32x4 e[14];
 #pragma unroll
-  for (int j = 0; j < nb; ++j) f[j] = lut[(wv[j >> 2] >> (8 * (j & 3))) & 0xFFu];
+  for (int j = 0; j < nb; ++j)
+    e[j] = *reinterpret_cast<const u32x4*>(lut + 4 * ((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu));
 #pragma unroll
   for (int t = 0; t < NC / 2; ++t) {
-    uint32_t h[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int c = S::c0 + 2 * t + e;
-      const int j = t5_byte_of<GS>(c) - S::start;
-      const int d = t5_digit_of<GS>(c);
-      const uint32_t shift = (f[j] >> (6 * d)) & 63u;
-      h[e] = (uint32_t)(wt >> shift) & 0xFFFFu;
+    const int ca = S::c0 + 2 * t, cb = ca + 1;
+    const int ja = t5_byte_of<GS>(ca) - S::start, jb = t5_byte_of<GS>(cb) - S::start;
+    const int ia = t5_digit_of<GS>(ca);
+    uint32_t sel;
+    if (ja == jb) {
+      // digits (ia, ia + 1) of one byte: entry 0, 2, 1 or 3 for ia = 0..3
+      sel = e[ja][ia == 0 ? 0 : ia == 1 ? 2 : ia == 2 ? 1 : 3];
+    } else {
+      // digit 4 of byte ja (high half of its entry 3), digit 0 of byte jb
+      // (low half of its entry 0)
+      sel = __builtin_amdgcn_alignbit(e[jb][0], e[ja][3], 16);
     }
-    out[t] = h[0] | (h[1] << 16);
+    out[t] = __builtin_amdgcn_perm(wt_hi, wt_lo, sel);
   }
 }
 
@@ -132,15 +149,15 @@ __device__ __forceinline__ int t5_span_start(int h) {
 }
 
 template <int GS, int PAR, int NC>
-__device__ __forceinline__ void t5_decode_h(int h, const uint32_t (&wv)[4], uint64_t wt, const uint32_t* lut,
-                                            uint32_t (&out)[NC / 2]) {
-  if (h == 0) t5_decode<GS, PAR, 0, NC>(wv, wt, lut, out);
+__device__ __forceinline__ void t5_decode_h(int h, const uint32_t (&wv)[4], uint32_t wt_lo, uint32_t wt_hi,
+                                            const uint32_t* lut, uint32_t (&out)[NC / 2]) {
+  if (h == 0) t5_decode<GS, PAR, 0, NC>(wv, wt_lo, wt_hi, lut, out);
   if constexpr (64 / NC > 1) {
-    if (h == 1) t5_decode<GS, PAR, 1, NC>(wv, wt, lut, out);
+    if (h == 1) t5_decode<GS, PAR, 1, NC>(wv, wt_lo, wt_hi, lut, out);
   }
   if constexpr (64 / NC > 2) {
-    if (h == 2) t5_decode<GS, PAR, 2, NC>(wv, wt, lut, out);
-    if (h == 3) t5_decode<GS, PAR, 3, NC>(wv, wt, lut, out);
+    if (h == 2) t5_decode<GS, PAR, 2, NC>(wv, wt_lo, wt_hi, lut, out);
+    if (h == 3) t5_decode<GS, PAR, 3, NC>(wv, wt_lo, wt_hi, lut, out);
   }
 }
 
@@ -158,7 +175,7 @@ template <int BN, int GS, bool IMPLIED>
 struct T5Decoder {
   static constexpr int NC = BN / 4;
   static constexpr int kRawLoads = IMPLIED ? 2 : 3;
-  static constexpr int kLutWords = 256;
+  static constexpr int kLutWords = 1024;  // 4 pair selectors per byte value
   static constexpr int P1 = GS == 128 ? 1 : 0;
   struct Raw {
     u32x4 d;
@@ -169,7 +186,7 @@ struct T5Decoder {
   int h;
 
   __device__ __forceinline__ static void init_lut(uint32_t* lut, int tid) {
-    if (tid < 256) lut[tid] = tid < 243 ? t5_shift_fields((uint32_t)tid) : 0u;
+    for (int e = tid; e < kLutWords; e += kQmmThreads) lut[e] = t5_pair_entry((uint32_t)(e >> 2), e & 3);
   }
   __device__ __forceinline__ T5Decoder(const QmmParams& p, int n, int h_) : h(h_) {
     rw = make_rsrc(p.w, p.w_bytes);
@@ -202,20 +219,23 @@ struct T5Decoder {
     uint32_t wv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) wv[k] = __builtin_amdgcn_alignbyte(k < 3 ? rw_.d[k + 1] : 0u, rw_.d[k], sh);
-    uint64_t wt;
+    // the row's weights for q = 0, 1, 2: {-s, 0, +s} exactly when the bias
+    // is -scale, else the correctly rounded s*q + b
+    uint32_t wt_lo, wt_hi;
     if constexpr (IMPLIED) {
-      const uint32_t sp = rw_.s, sn = rw_.s ^ 0x8000u;  // +s, -s (exact)
-      wt = (uint64_t)sn | ((uint64_t)sp << 32);
+      wt_lo = (uint32_t)(rw_.s ^ 0x8000u) & 0xFFFFu;  // -s, then +0
+      wt_hi = rw_.s;                                 // +s
     } else {
       const float s = h2f(__builtin_bit_cast(half_t, rw_.s)), b = h2f(__builtin_bit_cast(half_t, rw_.b));
       const uint32_t v0 = __builtin_bit_cast(uint16_t, affine_to_half(s, 0u, b));
       const uint32_t v1 = __builtin_bit_cast(uint16_t, affine_to_half(s, 1u, b));
       const uint32_t v2 = __builtin_bit_cast(uint16_t, affine_to_half(s, 2u, b));
-      wt = (uint64_t)(v0 | (v1 << 16)) | ((uint64_t)v2 << 32);
+      wt_lo = v0 | (v1 << 16);
+      wt_hi = v2;
     }
     const int par = GS == 128 ? (step & 1) : 0;
-    if (par == 0) t5_decode_h<GS, 0, NC>(h, wv, wt, lut, out);
-    else t5_decode_h<GS, P1, NC>(h, wv, wt, lut, out);
+    if (par == 0) t5_decode_h<GS, 0, NC>(h, wv, wt_lo, wt_hi, lut, out);
+    else t5_decode_h<GS, P1, NC>(h, wv, wt_lo, wt_hi, lut, out);
   }
 };
 
