@@ -66,7 +66,8 @@ def parse():
                     help="shapes (2-bit, gs=64, M=1) timed with the CPU oracle")
     ap.add_argument("--suite", default="", help="'full': also time M=1..5 wide/sym, t5 and qmm "
                     "configurations and write them to --detail-csv")
-    ap.add_argument("--detail-csv", default=os.path.join(ROOT, "gpurun_out", "bench_detail.csv"))
+    ap.add_argument("--detail-csv", default=os.path.join(ROOT, "results", "bench_detail.csv"),
+                    help="where --suite full writes its per-call table")
     ap.add_argument("--counters", action="store_true",
                     help="eager calibration copy and one cold launch per shape of the dominant kernel, for "
                          "rocprofv3 --pmc runs")
@@ -420,8 +421,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the QMV path has no multi-GPU mode in this build "
-              "(it would shard W along N with no communication); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the QMV path has no multi-GPU mode (it would shard W "
+              "along N with no communication); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

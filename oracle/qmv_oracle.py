@@ -19,7 +19,7 @@ Source of the method ("the article"): the web article "oMLX Bonsai
 * section 二, path 3 (t5) -- ternary codes {0,1,2} stored in uint8, 13/26
   bytes per weight group, about 1.585 bit per weight.
 
-Readings where the article is silent (each one is listed in the design doc):
+Readings where the article is silent:
 
 * R1 weight matrix is ``W[N][K]`` (output x input, the QuantizedLinear
   convention); groups of ``gs`` consecutive weights along K share one fp16

@@ -8,7 +8,7 @@ the HIP library.
 Source: the web article "oMLX Bonsai 自定义内核: Qwen 系列快速 QMV 路径完整
 解析", section 三: ``spec_decode_verify`` fuses three steps into one kernel --
 compare the draft tokens, count the accepted length, produce the correction
-token.  The article gives no formulas; reading R10 (listed in the design doc) is
+token.  The article gives no formulas; the reading taken here (R10) is
 greedy verification:
 
 * ``t[i] = argmax_v logits[i][v]`` for the L+1 positions the target model
