@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="eager calibration copy and one cold launch per shape of the dominant kernel, for "
                          "rocprofv3 --pmc runs")
+    ap.add_argument("--qmm-counters", action="store_true",
+                    help="one cold t5_qmm launch per prefill configuration (gs 128, gate and down, M 32, 512, "
+                         "2048), for rocprofv3 --pmc runs of the matrix-core counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="rocprofv3 counter_collection.csv files of --counters runs with FETCH_SIZE and "
                          "WRITE_SIZE; writes profiles/traffic.json")
@@ -363,6 +366,29 @@ def counter_run(torch, lib, dev):
     print(json.dumps({"counter_run": [c.label for c in calls], "bytes": [c.bytes for c in calls]}), flush=True)
 
 
+def qmm_counter_run(torch, lib, dev):
+    """Eager launches for matrix-core counter runs: t5_qmm (gs 128) on the
+    gate and down shapes at M = 32, 512, 2048, each after a pass over
+    CAL_BYTES that evicts the last-level cache."""
+    import synth
+    src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    specs = []
+    for shape in ("gate", "down"):
+        N, K = synth.PROJECTION_SHAPES[shape]
+        for M in (32, 512, 2048):
+            specs.append(("bq_t5_qmm", "t5", M, N, K, 128, "t5", f"t5_qmm/gs128/{shape}/M{M}"))
+    calls = make_calls(torch, dev, specs, copies=1)[0]
+    h = torch.cuda.current_stream().cuda_stream
+    for c in calls:
+        torch.add(src, 1.0, out=dst)  # evicts the last-level cache
+        torch.cuda.synchronize()
+        c.launch(lib, h)
+        torch.cuda.synchronize()
+    print(json.dumps({"qmm_counter_run": [c.label for c in calls],
+                      "flops": [2 * c.M * c.N * c.K for c in calls]}), flush=True)
+
+
 def traffic_from(fetch_csv, write_csv):
     """profiles/traffic.json from the counter_collection.csv files of two
     --counters runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)."""
@@ -438,6 +464,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.counters:
         counter_run(torch, lib, dev)
+        return
+    if args.qmm_counters:
+        qmm_counter_run(torch, lib, dev)
         return
 
     specs = []
