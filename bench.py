@@ -25,11 +25,18 @@ Extra objects on the JSON line:
                 from FETCH_SIZE + WRITE_SIZE counters, calibrated on a copy
                 kernel, when taken on the current kernel sources.
 
-Counter runs (under rocprofv3 --pmc, one counter per run):
-  python3 bench.py --counters              calibration copy + cold launches
-  python3 bench.py --traffic-from F.csv W.csv   writes profiles/traffic.json
-  cpu_baseline  the fp64 CPU oracle on a bounded sample (see --cpu-sample).
+  cpu_baseline  the fp64 CPU oracle on the dominant kernel's seven shapes
+                (see --cpu-sample), timed on the host.
   breakdown     per (bits, gs, shape) microseconds and GB/s.
+
+Other modes:
+  python3 bench.py --suite full            also M = 1..5 (affine, symmetric, per-row),
+                                           t5, qmm, repack and verify; CSV table
+  python3 bench.py --counters              calibration copy + cold decode launches
+                                           (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
+  python3 bench.py --traffic-from F.csv W.csv   writes profiles/traffic.json
+  python3 bench.py --qmm-counters          cold t5_qmm launches on the prefill
+                                           configurations (matrix-core counters)
 """
 from __future__ import annotations
 
