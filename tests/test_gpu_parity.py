@@ -308,10 +308,13 @@ def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
 
 
 @pytest.mark.parametrize("shape", ["gate", "down"])
-def test_t5_qmm_full_size_sampled(shape):
+@pytest.mark.parametrize("M", [32, 512, 2048])
+def test_t5_qmm_full_size_sampled(shape, M):
+    """The prefill configurations the benchmark times (gs 128, gate and
+    down, M 32 / 512 / 2048), checked on sampled output columns."""
     N, K = synth.PROJECTION_SHAPES[shape]
-    inp = make("t5", 32, N, K, 128, "t5", seed=21)
-    print(f"qmm full {shape}", flush=True)
+    inp = make("t5", M, N, K, 128, "t5", seed=21)
+    print(f"qmm full {shape} M{M}", flush=True)
     y = run_entry("t5_qmm", inp)
     assert np.all(np.isfinite(y))
     assert_close(y, inp, rows=_sample_rows(N, 22), what=f"qmm {shape}")

@@ -70,10 +70,11 @@ def test_qmm_one_hot_rows_read_exact_weights(fmt, gs, variant, M, N, K):
 
 @pytest.mark.parametrize("shape", ["gate", "down"])
 @pytest.mark.parametrize("fmt", ["u1", "u2"])
-def test_qmm_full_size_sampled(shape, fmt):
+@pytest.mark.parametrize("M", [32, 64, 2048])
+def test_qmm_full_size_sampled(shape, fmt, M):
     N, K = synth.PROJECTION_SHAPES[shape]
-    inp = make(fmt, 64, N, K, 128, "asym", seed=93)
-    print(f"qmm full {shape} {fmt}", flush=True)
+    inp = make(fmt, M, N, K, 128, "asym", seed=93)
+    print(f"qmm full {shape} {fmt} M{M}", flush=True)
     y = run_entry("qmm", inp)
     assert np.all(np.isfinite(y))
     assert_close(y, inp, rows=_sample_rows(N, 94), what=f"qmm {shape} {fmt}")
