@@ -339,14 +339,18 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
                        : launch_qmm_t<32, 128, BITS, GS, IMPLIED>(p, o->sub, stream);
   }
   // Rules from a measured sweep of every tile (MI355X, gate and down shapes,
-  // M 48 .. 2048), where the estimate below falls short:
-  // * when all 64 x 64 tiles run at once (one per CU), that tile with 4
-  //   steps per iteration (down: M = 96 213 -> 156 us, M = 128 215 -> 156);
+  // M 17 .. 2048), where the estimate below falls short:
+  // * when all 32 x 64 tiles run at once (one per CU), that tile with 4
+  //   steps per iteration (down: M = 48 214 -> 143 us, M = 96 213 -> 143);
+  // * else when all 64 x 64 tiles do, that tile with 4 steps per iteration
+  //   (down: M = 128 215 -> 156 us);
   // * with 256 to 512 tiles of 128 x 64 (two per CU, all resident) and more
   //   than 64 rows, that tile (down, M = 512: 295 -> 262 us); with fewer
   //   tiles it is slower than the estimate's choice.
+  const int t32 = ((p.M + 31) / 32) * ((p.N + 63) / 64);
   const int t64 = ((p.M + 63) / 64) * ((p.N + 63) / 64);
   const int t128 = ((p.M + 127) / 128) * ((p.N + 63) / 64);
+  if (steps % 4 == 0 && t32 <= 256) return launch_qmm_t<32, 64, BITS, GS, IMPLIED>(p, 4, stream);
   if (steps % 4 == 0 && t64 <= 256) return launch_qmm_t<64, 64, BITS, GS, IMPLIED>(p, 4, stream);
   if (p.M > 64 && t128 > 256 && t128 <= 512) return launch_qmm_t<128, 64, BITS, GS, IMPLIED>(p, 1, stream);
   const Cand* best = nullptr;
