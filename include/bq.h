@@ -84,11 +84,13 @@ typedef enum bq_status {
 
 /* bq_linear flags */
 #define BQ_LINEAR_SYM 1   /* bias implied (-scale*ratio; t5: -scale), biases never read */
-/* t5 calls of bq_linear with M >= BQ_T5_QMM_MIN_M take the fused qmm path */
+/* t5 calls of bq_linear with M >= BQ_T5_QMM_MIN_M take the fused qmm path
+ * when the product has at least BQ_QMM_MIN_TILES tiles (below) */
 #define BQ_T5_QMM_MIN_M 17
 /* 1/2-bit calls of bq_linear take bq_qmm when M >= BQ_QMM_MIN_M and the
  * product has at least BQ_QMM_MIN_TILES tiles of 32 x 64 outputs
- * (ceil(N/64)*ceil(M/32)), enough to occupy half the CUs */
+ * (ceil(N/64)*ceil(M/32)), enough to occupy half the CUs; the same tile
+ * count gates the t5 fused path */
 #define BQ_QMM_MIN_M 17
 #define BQ_QMM_MIN_TILES 128
 
@@ -96,7 +98,7 @@ typedef enum bq_route {
   BQ_ROUTE_QMV_WIDE = 1,  /* bits 1/2, stored bias: bq_qmv_wide per pass of <= 5 rows */
   BQ_ROUTE_QMV_SYM = 2,   /* bits 1/2, implied bias: bq_qmv_sym per pass of <= 5 rows */
   BQ_ROUTE_T5_WIDE = 3,   /* t5: bq_t5_qmv_wide per pass of <= 5 rows */
-  BQ_ROUTE_T5_QMM = 4,    /* t5, M >= BQ_T5_QMM_MIN_M: one bq_t5_qmm */
+  BQ_ROUTE_T5_QMM = 4,    /* t5, M >= BQ_T5_QMM_MIN_M and tiles as below: one bq_t5_qmm */
   BQ_ROUTE_QMM = 5        /* bits 1/2, M and tiles as above: one bq_qmm */
 } bq_route;
 
@@ -171,9 +173,9 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
  *             BQ_QMM_MIN_TILES tiles, else passes of up to 5 rows through
  *             bq_qmv_wide, or bq_qmv_sym when flags has BQ_LINEAR_SYM (each
  *             pass reads W once; M > 5 reads it ceil(M/5) times);
- *   t5:       M < BQ_T5_QMM_MIN_M: passes of up to 5 rows through
- *             bq_t5_qmv_wide; M >= BQ_T5_QMM_MIN_M: bq_t5_qmm (the
- *             article's prefill rule, M > 16).
+ *   t5:       bq_t5_qmm when M >= BQ_T5_QMM_MIN_M (the article's prefill
+ *             rule, M > 16) and the product has BQ_QMM_MIN_TILES tiles,
+ *             else passes of up to 5 rows through bq_t5_qmv_wide.
  * Arguments as for the entry point a pass goes to; with BQ_LINEAR_SYM the
  * biases argument is ignored (may be NULL) and the bias is implied.
  * Results are those of the entry points the passes take; each pass is

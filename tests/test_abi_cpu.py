@@ -231,13 +231,16 @@ def test_linear_routes():
         assert bq.bq_linear_route(17, 64 * 127, bits) == ("qmv_wide", 4)
         assert bq.bq_linear_route(2048, down, bits) == ("qmm", 1)
     # t5: wide passes below 17 rows, the fused product from 17 (M > 16)
+    # when there are 128 tiles of 32 x 64, as for bits 1/2
     assert bq.T5_QMM_MIN_M == 17
     for M in (1, 5):
         assert bq.bq_linear_route(M, gate, bq.BITS_T5) == ("t5_qmv_wide", 1)
         assert bq.bq_linear_route(M, gate, bq.BITS_T5, bq.LINEAR_SYM) == ("t5_qmv_wide", 1)
     assert bq.bq_linear_route(16, gate, bq.BITS_T5) == ("t5_qmv_wide", 4)
     assert bq.bq_linear_route(17, gate, bq.BITS_T5) == ("t5_qmm", 1)
-    assert bq.bq_linear_route(17, 64, bq.BITS_T5) == ("t5_qmm", 1)
+    assert bq.bq_linear_route(17, 64, bq.BITS_T5) == ("t5_qmv_wide", 4)    # 1 tile
+    assert bq.bq_linear_route(17, down, bq.BITS_T5) == ("t5_qmv_wide", 4)  # 80 tiles
+    assert bq.bq_linear_route(33, down, bq.BITS_T5) == ("t5_qmm", 1)       # 160 tiles
     assert bq.bq_linear_route(512, gate, bq.BITS_T5) == ("t5_qmm", 1)
 
 

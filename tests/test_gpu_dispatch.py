@@ -166,3 +166,27 @@ def test_linear_1_2_bit_prefill_routes(fmt, gs, M, NN):
         ref = np.concatenate([to_np(bq.qmv_wide(x[m0:m0 + 5].contiguous(), qw.w, qw.scales, qw.biases, bits, gs))
                               for m0 in range(0, M, 5)])
     assert np.array_equal(y.view(np.uint16), ref.view(np.uint16)), route
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M,NN", [(17, 8192), (16, 8192), (17, 5120), (40, 5120)])
+def test_linear_t5_prefill_routes(gs, M, NN):
+    """t5 from 17 rows takes the fused product when it has 128 tiles of
+    32 x 64 (17 x 8192, 40 x 5120) and gives its bits; otherwise (16 rows,
+    or 17 x 5120 with 80 tiles) five-row wide passes."""
+    bq, torch = _bq()
+    inp = make("t5", M, NN, 1024, gs, seed=102)
+    qw = _qw(bq, inp, biases=None)
+    x = dev(inp.x)
+    y = to_np(bq.linear(x, qw))
+    torch.cuda.synchronize()
+    assert_close(y.astype(np.float64), inp, rows=np.arange(0, NN, 97), what=f"linear t5 M{M} N{NN}")
+    route, passes = bq.bq_linear_route(M, NN, bq.BITS_T5)
+    expect = "t5_qmm" if (NN + 63) // 64 * ((M + 31) // 32) >= 128 and M >= 17 else "t5_qmv_wide"
+    assert route == expect
+    if route == "t5_qmm":
+        ref = to_np(bq.t5_qmm(x, qw.w, qw.scales, gs))
+    else:
+        ref = np.concatenate([to_np(bq.t5_qmv_wide(x[m0:m0 + 5].contiguous(), qw.w, qw.scales, gs))
+                              for m0 in range(0, M, 5)])
+    assert np.array_equal(y.view(np.uint16), ref.view(np.uint16)), route
