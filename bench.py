@@ -212,18 +212,13 @@ def cpu_baseline(shapes):
 
 
 def kernel_source_hash():
-    """Hash of the decode kernel's own sources: qmv_kernels.hpp and the
-    qmv-family launch section of bq_api.hip (geometry and launch
-    configuration).  Counter results are tied to it."""
+    """Hash of the decode kernel's own sources: qmv_kernels.hpp and its host
+    launch configuration (qmv_launch.hpp).  Counter results are tied to it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_decode_qmv_amd", "csrc")
-    with open(os.path.join(csrc, "qmv_kernels.hpp"), "rb") as f:
-        h.update(f.read())
-    with open(os.path.join(csrc, "bq_api.hip"), "r", encoding="utf-8") as f:
-        api = f.read()
-    start = api.index("// ---------------------------------------------------------------- qmv family")
-    end = api.index("// ---------------------------------------------------------------- qmm")
-    h.update(api[start:end].encode())
+    for name in ("qmv_kernels.hpp", "qmv_launch.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -1,23 +1,27 @@
-"""Compile the HIP library (libbq.so) in-tree for gfx950 with hipcc."""
+"""Compile the HIP library (libbq.so) in-tree for gfx950 with hipcc.
+
+The kernel instances of each weight format sit in translation units of
+their own; they compile in parallel and are linked into one shared library.
+"""
 from __future__ import annotations
 
 import os
 import shutil
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libbq.so")
-SOURCES = ["bq_api.hip"]
-HEADERS = ["qmv_kernels.hpp", "dequant_kernels.hpp", "qmm_kernels.hpp", "sym_kernels.hpp", "repack_kernels.hpp"]
+SOURCES = ["bq_api.hip", "qmv_u1.hip", "qmv_u2.hip", "qmv_t5.hip", "qmm_u1.hip", "qmm_u2.hip", "qmm_t5.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
-    "-shared",
     "-fPIC",
     # packed fp32 arithmetic stays off in all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,16 +37,27 @@ def hipcc() -> str:
     return path
 
 
-def build_library(verbose: bool = False) -> str:
-    """Always recompiles; returns the path of the built library."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return res
+
+
+def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+    """Always recompiles; returns the path of the built library."""
+    cc = hipcc()
+    jobs = jobs or min(len(SOURCES), max(1, len(os.sched_getaffinity(0))))
+    with tempfile.TemporaryDirectory(prefix="bq_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB_PATH + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -1,0 +1,10 @@
+// Prefill product instances of one weight format.
+#include "qmm_launch.hpp"
+
+namespace bq {
+
+int launch_qmm_u1(const QmmParams& p, int gs, bool implied, void* stream) {
+  return launch_qmm_bits<1>(p, gs, implied, stream);
+}
+
+}  // namespace bq

@@ -1,0 +1,11 @@
+// Decode kernel instances of one weight format.
+#include "qmv_launch.hpp"
+
+namespace bq {
+
+QmvLauncher pick_qmv_u2(int gs, int M, bool implied) {
+  if (gs == 64) return implied ? pick_m<FMT_U2, 64, true>(M) : pick_m<FMT_U2, 64, false>(M);
+  return implied ? pick_m<FMT_U2, 128, true>(M) : pick_m<FMT_U2, 128, false>(M);
+}
+
+}  // namespace bq
