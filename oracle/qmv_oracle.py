@@ -39,7 +39,6 @@ Every function computes in float64 from exactly converted fp16 inputs.
 from __future__ import annotations
 
 import math
-from fractions import Fraction
 
 import numpy as np
 
@@ -211,7 +210,8 @@ def qmv_f64(x: np.ndarray, W64: np.ndarray) -> np.ndarray:
 
 
 def abs_mass(x: np.ndarray, W64: np.ndarray) -> np.ndarray:
-    """``sum_k |x[m][k] * W[n][k]|`` -- the scale of the acceptance bound."""
+    """``sum_k |x[m][k] * W[n][k]|`` -- the scale of the acceptance bound
+    (reading R5): the sum of the element-wise absolute products."""
     return np.abs(np.asarray(x, dtype=np.float16).astype(np.float64)) @ np.abs(W64).T
 
 
@@ -233,23 +233,6 @@ def qmv_brute(x, codes, scales, biases_f64, group_size):
                 g = k // group_size
                 wk = float(scales[n][g]) * float(codes[n][k]) + float(biases_f64[n][g])
                 acc += float(x[m][k]) * wk
-            y[m][n] = acc
-    return y
-
-
-def qmv_exact(x, codes, scales, biases_f64, group_size):
-    """Exact rational result (tiny inputs): every fp16/fp64 input is a dyadic
-    rational, so this is the true value the fp64 oracle must round to."""
-    M, K = len(x), len(x[0])
-    N = len(codes)
-    y = [[Fraction(0)] * N for _ in range(M)]
-    for m in range(M):
-        for n in range(N):
-            acc = Fraction(0)
-            for k in range(K):
-                g = k // group_size
-                wk = Fraction(float(scales[n][g])) * int(codes[n][k]) + Fraction(float(biases_f64[n][g]))
-                acc += Fraction(float(x[m][k])) * wk
             y[m][n] = acc
     return y
 

@@ -63,8 +63,9 @@ def pin_article_facts():
     for gs in (64, 128):
         assert Q.t5_group_bytes(gs) * 8 / gs == pytest.approx(1.625)
     assert math.log2(3) == pytest.approx(1.585, abs=5e-4)
-    # section 二 path 3: "about 23% less RAM than 2-bit uint32" -- holds when
-    # t5 stores one fp16 scale per group and 2-bit stores scale + bias:
+    # section 二 path 3 puts t5's memory about a quarter below 2-bit uint32
+    # weights; that holds when t5 stores one fp16 scale per group and 2-bit
+    # stores scale + bias:
     for gs, lo, hi in ((64, 0.2, 0.26), (128, 0.2, 0.26)):
         t5 = Q.algorithmic_bytes("t5", 0, 1, 1024 * gs, gs, bias_stored=False)
         u2 = Q.algorithmic_bytes("u2", 0, 1, 1024 * gs, gs, bias_stored=True)
@@ -251,10 +252,48 @@ def pin_tolerance_rule():
     assert not ok
 
 
+def pin_abs_mass():
+    """The bound's scale term is the sum of the element-wise absolute
+    products (hand-worked values in tests/golden/abs_mass.json), not the
+    absolute sum, not the product of the norms, not a sum with signed x."""
+    g = _load("abs_mass.json")
+    c = g["plain"]
+    x = np.array(c["x"], np.float16)
+    W = np.array(c["w"], np.float64)
+    assert Q.abs_mass(x, W).tolist() == [[c["mass"]]]
+    assert Q.qmv_f64(x, W).tolist() == [[c["y"]]]
+    c = g["u2"]
+    K, gs = c["K"], c["group_size"]
+    codes = np.full((1, K), c["codes_rest"], np.uint8)
+    codes[0, :4] = c["codes_head"]
+    x = np.zeros((1, K), np.float16)
+    x[0, :4] = c["x_head"]
+    y, mass = Q.qmv_reference("u2", x, Q.pack_words(codes, 2), np.array([[c["scale"]]], np.float16),
+                              np.array([[c["bias"]]], np.float16), K, gs)
+    assert y.tolist() == [[c["y"]]] and mass.tolist() == [[c["mass"]]], (y, mass)
+    c = g["t5"]
+    K, gs = c["K"], c["group_size"]
+    x = np.zeros((1, K), np.float16)
+    x[0, :6] = c["x_head"]
+    y, mass = Q.qmv_reference("t5", x, np.array([c["bytes"]], np.uint8), np.array([[c["scale"]]], np.float16),
+                              None, K, gs)
+    assert y.tolist() == [[c["y"]]] and mass.tolist() == [[c["mass"]]], (y, mass)
+    # invariants: one-hot x gives |w_k|; the mass bounds |y|; it does not see signs
+    rng = np.random.default_rng(14)
+    W = rng.uniform(-1, 1, (4, 64))
+    xr = synth.draw_x(rng, 3, 64)
+    m = Q.abs_mass(xr, W)
+    assert (m >= np.abs(Q.qmv_f64(xr, W)) - 1e-12).all()
+    assert np.array_equal(m, Q.abs_mass(-xr, W)) and np.array_equal(m, Q.abs_mass(xr, -W))
+    e = np.zeros((1, 64), np.float16)
+    e[0, 9] = 1.0
+    assert np.array_equal(Q.abs_mass(e, W)[0], np.abs(W[:, 9]))
+
+
 PINS = [pin_golden_words, pin_golden_t5, pin_article_facts, pin_golden_qmv_u2, pin_golden_qmv_t5,
         pin_golden_dequant_rne, pin_roundtrip, pin_scalar_vs_vector, pin_exact_rational,
         pin_brute_force, pin_one_hot, pin_constant_codes, pin_sym_identity, pin_t5_equals_u2,
-        pin_invalid_t5_rejected, pin_tolerance_rule]
+        pin_invalid_t5_rejected, pin_tolerance_rule, pin_abs_mass]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -329,6 +368,19 @@ def _loose_tolerance(y_ref, mass):
     return 1e-2 * mass + 1e-3 * np.abs(y_ref)
 
 
+def _mass_of_sum(x, W64):
+    return np.abs(Q.qmv_f64(x, W64))
+
+
+def _mass_product_of_norms(x, W64):
+    xa = np.abs(np.asarray(x, dtype=np.float16).astype(np.float64)).sum(axis=1, keepdims=True)
+    return xa * np.abs(W64).sum(axis=1)[None, :]
+
+
+def _mass_signed_x(x, W64):
+    return np.asarray(x, dtype=np.float16).astype(np.float64) @ np.abs(W64).T
+
+
 MUTANTS = {
     "msb_first_words": ("unpack_words", _msb_first_unpack),
     "msd_first_t5": ("t5_unpack", _msd_first_t5),
@@ -340,6 +392,9 @@ MUTANTS = {
     "dropped_bias": ("dequant_f64", _drop_bias),
     "half_up_rounding": ("dequant_f16", _half_up_round),
     "loose_tolerance": ("tolerance", _loose_tolerance),
+    "mass_of_sum": ("abs_mass", _mass_of_sum),
+    "mass_product_of_norms": ("abs_mass", _mass_product_of_norms),
+    "mass_signed_x": ("abs_mass", _mass_signed_x),
 }
 
 
