@@ -29,14 +29,19 @@
 //   for x never waits for W.
 // * Scaled codes: a code masked in place inside a 16-bit half reads as the
 //   fp16 subnormal q * 2^e * 2^-24, e its bit offset in the half;
-//   v_dot2_f32_f16 multiplies it by the staged x*2^-e, so every product is
-//   q*x*2^-24 exactly (up to the fp16 rounding of x*2^-e when
-//   |x| < 2^(e-14)), with no per-code conversion; 2^24 goes into the scale.
+//   v_dot2_f32_f16 multiplies it by the staged x*2^(c-e), so every product
+//   is q*x*2^(c-24) exactly, with no per-code conversion.  c is a power-of-
+//   two exponent chosen per staged chunk from its largest |x| (E = that
+//   value's fp16 exponent field, c = min(29 - E, 15)): the largest value
+//   lands in [2^14, 2^15), or a chunk below 1/2 is scaled by 2^15, so the
+//   staged fp16 values stay exact for every input magnitude fp16 can hold
+//   (elements below 2^-19 of their chunk's largest excepted), and the
+//   result scales with x.  2^-c multiplies the chunk's product sum.
 // * t5 bytes go through a 256-entry LDS table that holds a byte's five
 //   base-3 digits as 2-bit fields; two bytes fill one dword and five masks
 //   give five half2 code pairs.  13-byte runs are loaded as one dword-aligned
 //   16-byte window and realigned with v_alignbyte_b32.
-// * Epilogue per chunk: acc = fma(s*2^24, P, fma(b, X, acc)) in fp32 with X
+// * Epilogue per chunk: b*X + s*(P*2^-c) in fp32 (units of 2^-24), with X
 //   the chunk's (or, for 128-groups, the group's) sum of x.
 #pragma once
 
@@ -227,13 +232,26 @@ __device__ __forceinline__ uint32_t pair_halves(uint32_t a, int h, uint32_t b, i
   return lo | hi;
 }
 
-// (lo, hi) fp16 pair times 2^-e (exact unless the result is subnormal, then
-// rounded to nearest even, as one fp16 rounding of x*2^-e).
-__device__ __forceinline__ uint32_t scale_pair(uint32_t v, int e) {
+// (lo, hi) fp16 pair times 2^k, -14 <= k <= 15 (one fp16 rounding, to
+// nearest even, of the exact product).
+__device__ __forceinline__ uint32_t scale_pair(uint32_t v, int k) {
   const half2_t f = __builtin_bit_cast(half2_t, v);
-  const half_t sc = (half_t)__builtin_ldexpf(1.0f, -e);
+  const half_t sc = __builtin_bit_cast(half_t, (uint16_t)((k + 15) << 10));
   const half2_t r = f * half2_t{sc, sc};
   return __builtin_bit_cast(uint32_t, r);
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Staging exponent of a chunk whose largest |x| has the fp16 magnitude bits
+// amax: c = min(29 - E, 15), E = amax's exponent field.  Then the largest
+// value times 2^c lies in [2^14, 2^15) (for E >= 14), and x * 2^(c-e) for
+// a code offset e <= 9 is exact in fp16 unless |x| is below 2^-19 of the
+// chunk's largest; chunks below 1/2 get c = 15, where x * 2^(15-e) is
+// exact for every fp16 x (subnormal inputs are multiples of 2^-24).
+__device__ __forceinline__ int stage_exponent(uint32_t amax) {
+  const int E = (int)(amax >> 10);
+  return 29 - E < 15 ? 29 - E : 15;
 }
 
 // t5 digit table entry: digit i of byte v at bits 2i..2i+1.
@@ -334,16 +352,24 @@ __device__ __forceinline__ void xstage_load(rsrc_t rx, XStage<FMT, GS>& st) {
 }
 
 template <int FMT, int GS, int M>
-__device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_t* xs, float* xsum) {
+__device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_t* xs, float2* xsum) {
   if (!st.live) return;
   const int c = st.c;
   // X[j] = (x[2j], x[2j+1]) of the loaded span
   auto X = [&](int j) -> uint32_t { return j < 32 ? st.v[j >> 2][j & 3] : st.tail; };
   auto H = [&](int k) -> uint32_t { return (X(k >> 1) >> (16 * (k & 1))) & 0xFFFFu; };  // x[k] bits
-  auto P2 = [&](int k0_, int k1_, int e) -> uint32_t {  // (x[k0], x[k1]) * 2^-e; k < 0 means 0
+  // the chunk's staging exponent, from the largest |x| of the loaded span
+  // (for a t5 128-group half a value or two of the neighbouring half may
+  // take part: any exponent is exact as long as staging and epilogue agree)
+  u16x2 am = u16x2{0, 0};
+#pragma unroll
+  for (int j = 0; j < (XSpan<FMT, GS>::TAIL ? 33 : 32); ++j)
+    am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2, X(j) & 0x7FFF7FFFu));
+  const int ce = stage_exponent(am[0] > am[1] ? am[0] : am[1]);
+  auto P2 = [&](int k0_, int k1_, int e) -> uint32_t {  // (x[k0], x[k1]) * 2^(ce-e); k < 0 means 0
     const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
     const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
-    return scale_pair(lo | (hi << 16), e);
+    return scale_pair(lo | (hi << 16), ce - e);
   };
   uint32_t out[36];
 #pragma unroll
@@ -424,7 +450,9 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
 #pragma unroll
   for (int q = 0; q < 9; ++q)
     *reinterpret_cast<u32x4*>(dst + 4 * q) = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-  xsum[st.xi] = sum * 5.9604644775390625e-08f;  // * 2^-24, like the products
+  // the sum * 2^-24 (the units of the products) and the factor 2^-ce that
+  // brings the chunk's products to those units
+  xsum[st.xi] = float2{sum * 5.9604644775390625e-08f, __builtin_bit_cast(float, (uint32_t)(127 - ce) << 23)};
 }
 
 // --------------------------------------------------------------------------
@@ -615,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   const int ST = p.seg_tiles;
   const int T = p.ntiles;
   uint32_t* xs = smem;                                              // [ST*16][CS]
-  float* xsum = reinterpret_cast<float*>(smem + ST * kKL * CS);     // [ST*16][M]
+  float2* xsum = reinterpret_cast<float2*>(smem + ST * kKL * CS);   // [ST*16][M]
   uint32_t* sbl = reinterpret_cast<uint32_t*>(xsum + ST * kKL * M);  // [sb_dwords]
   constexpr bool SBF = sb_f32<M>();
   float* part = reinterpret_cast<float*>(sbl + p.sb_dwords);        // [NG*T][R*M]
@@ -726,14 +754,18 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
 #pragma unroll
       for (int m = 0; m < M; ++m) Pd[r][m] = 0.f;
     chunk_dot<FMT, M, R>(wc, xs + cs * CS, lut, sh, Pd);
-    float X[M];
+    float X[M], F[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) X[m] = xsum[cs * M + m];
+    for (int m = 0; m < M; ++m) {
+      const float2 xf = xsum[cs * M + m];
+      X[m] = xf.x;
+      F[m] = xf.y;
+    }
     float v[R * M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < M; ++m) v[r * M + m] = __builtin_fmaf(bb[r], X[m], sc[r] * Pd[r][m]);
+      for (int m = 0; m < M; ++m) v[r * M + m] = __builtin_fmaf(bb[r], X[m], sc[r] * (Pd[r][m] * F[m]));
     rows_sum16<R * M>(v);
     if (kl == kKL - 1) {
       float* dst = part + (cg * T + tile) * (R * M);

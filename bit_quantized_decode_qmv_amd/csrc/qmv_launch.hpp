@@ -17,7 +17,7 @@ constexpr size_t kLdsBudget = 150 * 1024;
 size_t qmv_lds_bytes(int M, int R, int rows_per_wg, int ntiles, int seg_tiles, int G) {
   const size_t U = (size_t)((rows_per_wg + R - 1) / R) * ntiles;
   const size_t cs = (size_t)M * kXD + ((M % 2 == 0) ? 4 : 0);
-  return 4 * ((size_t)seg_tiles * kKL * cs + (size_t)M * seg_tiles * kKL +
+  return 4 * ((size_t)seg_tiles * kKL * cs + 2 * (size_t)M * seg_tiles * kKL +
               8 * (size_t)sb_entry_dwords(M) * sb_vectors(rows_per_wg, G) + U * R * M);
 }
 
