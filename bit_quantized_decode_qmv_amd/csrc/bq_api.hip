@@ -54,16 +54,17 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
     if (M < 1) return BQ_ERR_M;
     if ((e == E_WIDE || e == E_SYM || e == E_T5_WIDE) && M > BQ_MAX_WIDE_M) return BQ_ERR_M;
   }
-  if (!aligned(w, 4) || !aligned(scales, 2) || (biases && !aligned(biases, 2))) return BQ_ERR_ALIGN;
-  if (x && !aligned(x, 2)) return BQ_ERR_ALIGN;
-  if (!aligned(y, 2)) return BQ_ERR_ALIGN;
-  if (bits == BQ_BITS_T5 && K % 256 != 0) return BQ_ERR_ALIGN;
-  if (e != E_DEQUANT && !aligned(x, 16)) return BQ_ERR_ALIGN;
-  // the decode kernels read scales and biases in 16-byte vectors
-  if (e != E_DEQUANT && !mm &&
-      (!aligned(scales, 16) || (biases && e != E_SYM && !aligned(biases, 16))))
+  // Alignment: W and, for the decode calls, x, scales and biases (read as
+  // dwords) 4 bytes; the prefill products stage x with 16-byte loads that
+  // write LDS directly and need x 16-byte aligned; fp16 arrays read or
+  // written element by element 2 bytes.  A symmetric call never reads its
+  // biases, so their alignment does not matter there.
+  const bool decode = (e != E_DEQUANT && !mm);
+  const uintptr_t sb_align = decode ? 4 : 2;
+  if (!aligned(w, 4) || !aligned(scales, sb_align) || (biases && e != E_SYM && !aligned(biases, sb_align)))
     return BQ_ERR_ALIGN;
-  if (e == E_DEQUANT && bits != BQ_BITS_T5 && !aligned(y, 16)) return BQ_ERR_ALIGN;
+  if (x && !aligned(x, mm ? 16 : (decode ? 4 : 2))) return BQ_ERR_ALIGN;
+  if (!aligned(y, 2)) return BQ_ERR_ALIGN;
   return BQ_OK;
 }
 
@@ -73,6 +74,28 @@ size_t spec_workspace_bytes(int B, int L) { return spec_keys_bytes(B, L) + (size
 
 int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, void* params) {
   return launch_kernel(fn, grid, block, shmem, stream, params);
+}
+
+// dequant kernel instances by output alignment (16, 4 or 2 bytes)
+template <int BITS>
+const void* pick_dequant_words(bool implied, int A) {
+  if (implied)
+    return A == 16 ? reinterpret_cast<const void*>(&dequant_words_kernel<BITS, true, 16>)
+         : A == 4  ? reinterpret_cast<const void*>(&dequant_words_kernel<BITS, true, 4>)
+                   : reinterpret_cast<const void*>(&dequant_words_kernel<BITS, true, 2>);
+  return A == 16 ? reinterpret_cast<const void*>(&dequant_words_kernel<BITS, false, 16>)
+       : A == 4  ? reinterpret_cast<const void*>(&dequant_words_kernel<BITS, false, 4>)
+                 : reinterpret_cast<const void*>(&dequant_words_kernel<BITS, false, 2>);
+}
+template <int GS>
+const void* pick_dequant_t5(bool implied, int A) {
+  if (implied)
+    return A == 16 ? reinterpret_cast<const void*>(&dequant_t5_kernel<GS, true, 16>)
+         : A == 4  ? reinterpret_cast<const void*>(&dequant_t5_kernel<GS, true, 4>)
+                   : reinterpret_cast<const void*>(&dequant_t5_kernel<GS, true, 2>);
+  return A == 16 ? reinterpret_cast<const void*>(&dequant_t5_kernel<GS, false, 16>)
+       : A == 4  ? reinterpret_cast<const void*>(&dequant_t5_kernel<GS, false, 4>)
+                 : reinterpret_cast<const void*>(&dequant_t5_kernel<GS, false, 2>);
 }
 
 // ---------------------------------------------------------------- qmv family
@@ -157,8 +180,8 @@ const char* bq_strerror(int status) {
       return "N and K must be positive, K a multiple of group_size, and the sizes within the limits of bq.h";
     case BQ_ERR_M: return "M is outside the range this entry point accepts";
     case BQ_ERR_ALIGN:
-      return "a pointer is misaligned (x, and for the decode calls scales and biases, need 16 bytes), or a t5 "
-             "call has K not a multiple of 256";
+      return "a pointer is misaligned (W 4 bytes; x, scales and biases of the decode calls 4 bytes; x of the "
+             "prefill products 16 bytes; fp16 outputs 2 bytes), or a t5 repack has K not a multiple of 256";
     case BQ_ERR_FLAGS: return "flags holds bits this entry point does not define";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case BQ_ERR_WORKSPACE: return "the workspace is NULL or smaller than bq_spec_verify_workspace reports";
@@ -221,20 +244,16 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
   p.row_bytes = row_bytes_of(bits, K, group_size);
   p.ratio = bits == BQ_BITS_T5 ? 1.0f : (bits == 1 ? 0.5f : 1.5f);
   const bool implied = (biases == nullptr);
+  // widest stores the output's alignment allows
+  const int A = aligned(y, 16) ? 16 : (aligned(y, 4) ? 4 : 2);
   size_t items;
   const void* fn;
   if (bits == BQ_BITS_T5) {
-    items = (size_t)N * p.G * ((group_size + 4) / 5);
-    fn = implied ? reinterpret_cast<const void*>(&dequant_t5_kernel<true>)
-                 : reinterpret_cast<const void*>(&dequant_t5_kernel<false>);
+    items = (size_t)N * p.G;  // one thread per group
+    fn = group_size == 64 ? pick_dequant_t5<64>(implied, A) : pick_dequant_t5<128>(implied, A);
   } else {
-    items = (size_t)N * (K / (32 / bits));
-    if (bits == 1)
-      fn = implied ? reinterpret_cast<const void*>(&dequant_words_kernel<1, true>)
-                   : reinterpret_cast<const void*>(&dequant_words_kernel<1, false>);
-    else
-      fn = implied ? reinterpret_cast<const void*>(&dequant_words_kernel<2, true>)
-                   : reinterpret_cast<const void*>(&dequant_words_kernel<2, false>);
+    items = (size_t)N * (K / (32 / bits));  // one thread per word
+    fn = bits == 1 ? pick_dequant_words<1>(implied, A) : pick_dequant_words<2>(implied, A);
   }
   const size_t blocks = (items + 255) / 256;
   if (blocks > 0x7FFFFFFF) return BQ_ERR_SHAPE;

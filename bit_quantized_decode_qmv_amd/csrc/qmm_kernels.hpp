@@ -189,7 +189,8 @@ struct T5Decoder {
     for (int e = tid; e < kLutWords; e += kQmmThreads) lut[e] = t5_pair_entry((uint32_t)(e >> 2), e & 3);
   }
   __device__ __forceinline__ T5Decoder(const QmmParams& p, int n, int h_) : h(h_) {
-    rw = make_rsrc(p.w, p.w_bytes);
+    // whole dwords: the dword holding W's last byte is read in full
+    rw = make_rsrc(p.w, (p.w_bytes + 3) & ~3);
     rs = make_rsrc(p.s, p.sb_bytes);
     rb = make_rsrc(IMPLIED ? p.s : p.b, p.sb_bytes);
     row_off = (uint32_t)n * (uint32_t)p.row_bytes;

@@ -292,8 +292,8 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT>& c, rsrc_t w, uint32_t off
   } else if constexpr (FMT == FMT_U1) {
     c.v = __builtin_amdgcn_raw_buffer_load_b64(w, (int)off, 0, 0);
   } else {
-    // 13 bytes at off; rows are whole dwords, so the dword-aligned 16-byte
-    // window that holds them never passes the end of the row.
+    // 13 bytes at off, in the dword-aligned 16-byte window that holds them
+    // (past the end of W it reads zeros).
     c.v = __builtin_amdgcn_raw_buffer_load_b128(w, (int)(off & ~3u), 0, 0);
   }
 }
@@ -526,7 +526,7 @@ __device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl,
 // --------------------------------------------------------------------------
 template <int FMT, int M, int R>
 __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint32_t* xc,
-                                          const uint16_t* lut, uint32_t sh, float (&Pd)[R][M]) {
+                                          const uint16_t* lut, const uint32_t (&sh)[R], float (&Pd)[R][M]) {
   if constexpr (FMT == FMT_U2 || FMT == FMT_U1) {
     // quad q = 4 staged dwords 4q..4q+3 (2-bit: word q/2, pairs 4(q%2)..;
     // 1-bit: word q/4, pairs 4(q%4)..); the next quad's x is read while
@@ -577,14 +577,14 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
       pin_partials<R, M>(Pd);
     }
   } else {
-    // t5: realign each row's 13 bytes (they start `sh` bytes into the first
+    // t5: realign each row's 13 bytes (they start sh[r] bytes into the first
     // dword), then six byte pairs and the single byte 12 via the table
     uint32_t rb[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        rb[r][j] = __builtin_amdgcn_alignbyte(j < 3 ? wc[r].v[j + 1] : 0u, wc[r].v[j], sh);
+        rb[r][j] = __builtin_amdgcn_alignbyte(j < 3 ? wc[r].v[j + 1] : 0u, wc[r].v[j], sh[r]);
     }
     u32x4 xq[2][M];
     uint32_t x4[2][M];
@@ -654,8 +654,10 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   const int base = blockIdx.x * p.rows_per_wg;
   const int nrow_wg = min(p.rows_per_wg, p.N - base);
   const int NG = (nrow_wg + R - 1) / R;  // row-groups of this workgroup
-  const uint32_t sh = (uint32_t)(kl & 3);  // t5 run offset inside its first dword
-  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  // Descriptor sizes are rounded up to whole dwords: the range check zeroes
+  // every dword that reaches past the size, and the dword holding the last
+  // byte never leaves the page of a 4-byte aligned buffer.
+  const rsrc_t rw = make_rsrc(p.w, (p.w_bytes + 3) & ~3);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   // the workgroup's scale/bias block: bytes [sb_lo, sb_lo + nrow_wg*G*2)
   const uint32_t sb_lo = (uint32_t)base * (uint32_t)p.G * 2u;
@@ -669,11 +671,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   for (int k = 0; k < kStageRounds; ++k) xstage_plan<FMT, GS, M>(p, 0, min(ST, T), tid + k * kThreads, xst[k]);
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
-  // The range check zeroes whole dwords that reach past the descriptor's
-  // size, so the size is rounded up to the 16-byte block that holds the last
-  // element; with a 16-byte aligned base that block never leaves the page.
   SbStage sbst;
-  const int sb_size = (p.sb_bytes + 15) & ~15;
+  const int sb_size = (p.sb_bytes + 3) & ~3;
   sbstage_load<IMPLIED>(make_rsrc(p.s, sb_size), make_rsrc(IMPLIED ? p.s : p.b, sb_size), sb_lo_al, sb_nvec, sbst);
 
   auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
@@ -753,6 +752,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) Pd[r][m] = 0.f;
+    // t5 runs start 13 bytes apart: where each row's run sits in its dword
+    uint32_t sh[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      sh[r] = ((uint32_t)(base + cg * R + r) * (uint32_t)p.row_bytes + 13u * (uint32_t)chunk) & 3u;
     chunk_dot<FMT, M, R>(wc, xs + cs * CS, lut, sh, Pd);
     float X[M], F[M];
 #pragma unroll

@@ -40,17 +40,16 @@
  * names it.  A failed launch returns BQ_ERR_HIP.  Nothing aborts or throws
  * across this interface.
  *
- * Alignment: x needs 16-byte alignment (it is read in 16-byte vectors).
- * The decode calls (qmv, qmv_wide, qmv_sym, t5_qmv, t5_qmv_wide) also read
- * scales and biases in 16-byte vectors and need them 16-byte aligned
- * (qmv_sym ignores the bias pointer); bq_qmm, bq_t5_qmm and bq_dequant need
- * 2 bytes.
- * y needs 2-byte alignment, except that bq_dequant with bits 1/2 writes y in
- * 16-byte vectors and needs it 16-byte aligned; w needs 4-byte alignment
- * (uint32 words for bits 1/2; dword loads for t5).  Fresh allocations from
- * hipMalloc or torch meet all of these.  The t5 entry
- * points additionally need K to be a multiple of 256, so that every packed
- * row is a whole number of dwords (true of all the decoder shapes).
+ * Alignment: w needs 4-byte alignment (uint32 words for bits 1/2; dword
+ * loads for t5).  The decode calls (qmv, qmv_wide, qmv_sym, t5_qmv,
+ * t5_qmv_wide) read x, scales and biases as dwords and need them 4-byte
+ * aligned (qmv_sym ignores the bias pointer).  bq_qmm and bq_t5_qmm stage x
+ * with 16-byte loads that write LDS directly and need x 16-byte aligned,
+ * scales and biases 2-byte aligned.  y needs 2-byte alignment everywhere
+ * (bq_dequant uses 16-byte or dword stores when y allows them).  Fresh
+ * allocations from hipMalloc or torch meet all of these.  t5 weights need
+ * K to be a multiple of group_size only; rows need not be whole dwords
+ * (bq_t5_repack alone needs K to be a multiple of 256).
  */
 #ifndef BQ_H
 #define BQ_H
@@ -76,7 +75,7 @@ typedef enum bq_status {
                              a decode call with K / group_size > 4092 (a
                              workgroup's scales must fit its LDS) */
   BQ_ERR_M = -5,          /* M outside the range this entry point accepts */
-  BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or t5 with K % 256 != 0 */
+  BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or a t5 repack with K % 256 != 0 */
   BQ_ERR_HIP = -7,        /* the HIP runtime rejected a launch */
   BQ_ERR_FLAGS = -8,      /* bq_linear: flags holds undefined bits */
   BQ_ERR_WORKSPACE = -9   /* bq_spec_decode_verify: workspace NULL or too small */

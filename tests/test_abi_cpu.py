@@ -173,26 +173,22 @@ def test_alignment(lib, name):
         assert call(lib, name, bits=bits, x=PX + 1) == ALIGN
 
 
-def test_t5_needs_k_multiple_of_256(lib):
-    for name in T5_ENTRIES:
-        assert call(lib, name, bits=0, K=192) == ALIGN
-        assert call(lib, name, bits=0, K=384, gs=128) == ALIGN
-    assert call(lib, "bq_dequant", bits=0, K=192) == ALIGN
-
-
-def test_qmm_and_dequant_vector_alignment(lib):
+def test_qmm_x_vector_alignment(lib):
+    # the prefill products stage x with 16-byte loads that write LDS
     assert call(lib, "bq_t5_qmm", bits=0, x=PX + 8) == ALIGN
     assert call(lib, "bq_qmm", bits=1, x=PX + 8) == ALIGN
-    assert call(lib, "bq_dequant", bits=2, y=PY + 8) == ALIGN
+    assert call(lib, "bq_t5_qmm", bits=0, x=PX + 4) == ALIGN
 
 
 @pytest.mark.parametrize("name", ["bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide"])
-def test_decode_scale_bias_vector_alignment(lib, name):
-    # the decode kernels stage a workgroup's scales and biases with 16-byte loads
+def test_decode_dword_alignment(lib, name):
+    # the decode kernels read x, scales and biases as dwords (any 4-byte
+    # aligned address; the GPU tests run 4-byte offsets)
     bits = 0 if name in T5_ENTRIES else 2
-    assert call(lib, name, bits=bits, s=PS + 8) == ALIGN
+    assert call(lib, name, bits=bits, x=PX + 2) == ALIGN
+    assert call(lib, name, bits=bits, s=PS + 2) == ALIGN
     if name != "bq_qmv_sym":  # sym never reads the bias pointer
-        assert call(lib, name, bits=bits, b=PB + 8) == ALIGN
+        assert call(lib, name, bits=bits, b=PB + 2) == ALIGN
 
 
 def test_binding_raises_with_status(lib):
@@ -269,11 +265,11 @@ def test_linear_validates_before_launch(lib):
     assert lcall(lib, N=0) == SHAPE
     assert lcall(lib, x=None) == NULL
     assert lcall(lib, b=None) == NULL            # stored bias required without the sym flag
-    assert lcall(lib, x=PX + 8) == ALIGN
-    assert lcall(lib, s=PS + 8) == ALIGN
-    # t5 routes: wide below 17 rows, qmm from 17; both validate first
-    assert lcall(lib, bits=0, K=192, b=None) == ALIGN
-    assert lcall(lib, bits=0, M=17, K=192, b=None) == ALIGN
+    assert lcall(lib, x=PX + 2) == ALIGN
+    assert lcall(lib, s=PS + 2) == ALIGN
+    # t5 routes: wide below 17 rows (or with few output tiles), qmm from 17; both validate first
+    assert lcall(lib, bits=0, K=192, b=None, x=PX + 2) == ALIGN
+    assert lcall(lib, bits=0, M=17, N=8192, K=192, b=None, x=PX + 8) == ALIGN
     assert lcall(lib, bits=0, M=17, w=None, b=None) == NULL
     # the 1/2-bit fused route validates too, and needs stored biases without the sym flag
     assert lcall(lib, M=17, N=8192, b=None) == NULL
