@@ -1,42 +1,50 @@
 #!/usr/bin/env python3
 """Decode QMV benchmark on one MI355X.
 
-Workload (one step): the decode QMV of one hidden=5120 decoder layer at M=1
--- the seven projection shapes (q 6144x5120, k/v 1024x5120, o 5120x6144,
-gate/up 17408x5120, down 5120x17408) -- for bits 1 and 2 and group sizes 64
-and 128 (28 calls, affine weights with stored biases).  Inputs are seeded
-synthetic tensors already resident in HBM.  Every timed sequence rotates
-through enough distinct copies of its inputs (at least 512 MB) that the
-256 MB last-level cache cannot serve the weights from one launch to the
-next.
+Workload (one step): the decode QMV of one hidden=5120 decoder layer -- the
+seven projection shapes (q 6144x5120, k/v 1024x5120, o 5120x6144, gate/up
+17408x5120, down 5120x17408) -- at M = 1..5 activation rows, for 2-bit
+affine weights (stored biases, bq_qmv_wide), 2-bit symmetric weights (bias
+-1.5*scale implied and never read, bq_qmv_sym) and t5 ternary weights (bias
+-scale implied, bq_t5_qmv_wide), each at group sizes 64 and 128: 210 calls.
+Inputs are seeded synthetic tensors already resident in HBM.  The calls run
+M by M, and within one M through all 42 weight sets (about 550 MB), so no
+weight set is read again before every other one has been: the 256 MB
+last-level cache never serves weights from one launch to the next.
 
-value = algorithmic bytes of a step (packed W + scales + biases + x + y)
-        / measured step time, in GB/s.
+value = algorithmic bytes of a step (packed W + scales + biases [0 when
+        implied] + x + y) / measured step time, in GB/s.
 
-Each step is one HIP graph replay (the graph holds the 28 launches), so
+Each step is one HIP graph replay (the graph holds the 210 launches), so
 launch overhead from Python is not in the timed region.
 
 Extra objects on the JSON line:
-  roofline      the dominant kernel (2-bit, gs=64, M=1) over its seven shapes:
+  roofline      the dominant kernel family by time share of the step (one
+                format, group size, bias kind and M over the seven shapes):
                 algorithmic bytes per launch / average launch duration from
-                HIP events around graph replays of just those launches (the
-                duration is the launch period in the graph: kernel time plus
-                the gap to the next launch).  traffic: HBM bytes per launch
-                from FETCH_SIZE + WRITE_SIZE counters, calibrated on a copy
-                kernel, when taken on the current kernel sources.
-
-  cpu_baseline  the fp64 CPU oracle on the dominant kernel's seven shapes
-                (see --cpu-sample), timed on the host.
-  breakdown     per (bits, gs, shape) microseconds and GB/s.
+                HIP events around graph replays of just those launches,
+                rotating input copies (>= 512 MB).  traffic: HBM bytes per
+                launch from FETCH_SIZE + WRITE_SIZE counters, calibrated on a
+                copy kernel, when they were taken on the current kernel
+                sources (profiles/traffic.json).
+  cpu_baseline  the fp64 CPU oracle on the dominant family's seven shapes,
+                timed on the host cores.  The same leg checks sampled rows
+                of every timed call (outputs written by the timed buffers
+                before timing) against the oracle: "parity".
+  breakdown     per (format-variant, gs, M, shape) microseconds and GB/s,
+                each call timed alone over rotating input copies.
+  families      per (format-variant, gs, M): microseconds over the seven
+                shapes and share of the step.
 
 Other modes:
-  python3 bench.py --suite full            also M = 1..5 (affine, symmetric, per-row),
-                                           t5, qmm, repack and verify; CSV table
-  python3 bench.py --counters              calibration copy + cold decode launches
-                                           (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)
-  python3 bench.py --traffic-from F.csv W.csv   writes profiles/traffic.json
-  python3 bench.py --qmm-counters          cold t5_qmm launches on the prefill
-                                           configurations (matrix-core counters)
+  python3 bench.py --suite full            also 1-bit, per-row calls, qmm, dequant,
+                                           repack and verify; CSV table
+  python3 bench.py --launch-set NAME       eager launches for rocprofv3 --pmc runs:
+                                           one calibration copy, then each call of the
+                                           set once after a pass that evicts the cache
+  python3 bench.py --traffic-from F.csv W.csv --family KEY
+                                           writes profiles/traffic.json from two
+                                           --launch-set family:KEY counter runs
 """
 from __future__ import annotations
 
@@ -54,13 +62,14 @@ if ROOT not in sys.path:
 METRIC = "QMV achieved HBM GB/s (W+scales+biases+x) at M=1..5; % of MI355X peak"
 PEAK_HBM_GBS = 8000.0
 SHAPES = ("q", "k", "v", "o", "gate", "up", "down")
+MS = (1, 2, 3, 4, 5)
+GROUP_SIZES = (64, 128)
+# (format, variant, entry point): the three decode families of the step
+FAMILIES = (("u2", "asym", "bq_qmv_wide"), ("u2", "sym", "bq_qmv_sym"), ("t5", "t5", "bq_t5_qmv_wide"))
 COLD_BYTES = 512 << 20  # rotation set: twice the last-level cache
 CAL_BYTES = 256 << 20   # calibration copy: bytes read and bytes written
-DOMINANT = "qmv_u2_gs64_m1"
-
-
-def n_copies(bytes_per_copy):
-    return max(2, -(-COLD_BYTES // max(1, bytes_per_copy)))
+ENTRY_OF = {("u1", "asym"): "bq_qmv_wide", ("u1", "sym"): "bq_qmv_sym", ("u2", "asym"): "bq_qmv_wide",
+            ("u2", "sym"): "bq_qmv_sym", ("t5", "t5"): "bq_t5_qmv_wide", ("t5", "asym"): "bq_t5_qmv_wide"}
 
 
 def parse():
@@ -68,22 +77,22 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="q,k,v,o,gate,up,down",
-                    help="shapes (2-bit, gs=64, M=1) timed with the CPU oracle")
-    ap.add_argument("--suite", default="", help="'full': also time M=1..5 wide/sym, t5 and qmm "
-                    "configurations and write them to --detail-csv")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (oracle timing and the parity check of the timed calls)")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-call breakdown")
+    ap.add_argument("--suite", default="", help="'full': also time 1-bit, per-row, qmm, dequant, repack and "
+                    "verify configurations and write them to --detail-csv")
     ap.add_argument("--detail-csv", default=os.path.join(ROOT, "results", "bench_detail.csv"),
                     help="where --suite full writes its per-call table")
-    ap.add_argument("--counters", action="store_true",
-                    help="eager calibration copy and one cold launch per shape of the dominant kernel, for "
-                         "rocprofv3 --pmc runs")
-    ap.add_argument("--qmm-counters", action="store_true",
-                    help="one cold t5_qmm launch per prefill configuration (gs 128, gate and down, M 32, 512, "
-                         "2048), for rocprofv3 --pmc runs of the matrix-core counters")
+    ap.add_argument("--launch-set", default="",
+                    help="eager launches for rocprofv3 --pmc runs: 'family:KEY' (KEY like u2-asym/gs64/M5: the "
+                         "seven shapes), 'decode' (gate and down, M 1..5, 2-bit affine and t5, gs 64), 't5' (t5 "
+                         "gs 64 and 128, seven shapes, M 1 and 5), 'qmm' (t5 qmm gs 128 on gate and down, M 32, "
+                         "512, 2048), 'dequant' (bits 1, 2, t5 on gate and down)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="rocprofv3 counter_collection.csv files of --counters runs with FETCH_SIZE and "
-                         "WRITE_SIZE; writes profiles/traffic.json")
+                    help="rocprofv3 counter_collection.csv files of two --launch-set family:KEY runs with "
+                         "FETCH_SIZE and WRITE_SIZE; writes profiles/traffic.json")
+    ap.add_argument("--family", default="", help="family key for --traffic-from")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + steps only (for rocprofv3), skip the extra measurements")
     return ap.parse_args()
@@ -98,24 +107,57 @@ def algorithmic_bytes(fmt, M, N, K, gs, bias_stored):
     return w + N * G * 2 * (2 if bias_stored else 1) + M * K * 2 + M * N * 2
 
 
-class Call:
-    """One C ABI call on device-resident inputs."""
+def family_key(fmt, variant, gs, M):
+    return f"{fmt}-{variant}/gs{gs}/M{M}"
 
-    def __init__(self, entry, fmt, M, N, K, gs, tensors, label):
-        self.entry, self.fmt, self.M, self.N, self.K, self.gs = entry, fmt, M, N, K, gs
-        self.t = tensors  # keep alive
+
+class WeightSet:
+    """Host and device copies of one (format, variant, gs, shape) input set
+    drawn at M = 5; a call at M uses the first M rows of x."""
+
+    def __init__(self, torch, dev, fmt, variant, gs, shape):
+        import synth
+        self.fmt, self.variant, self.gs, self.shape = fmt, variant, gs, shape
+        self.N, self.K = synth.PROJECTION_SHAPES[shape]
+        self.host = synth.make_inputs(fmt, 5, self.N, self.K, gs, variant, seed=0)
+        h = self.host
+        self.dev = [upload(torch, a, dev) for a in (h.x, h.w, h.scales, h.biases)]
+
+
+class Call:
+    """One C ABI call on device-resident inputs (x rows 0..M-1 of its set)."""
+
+    def __init__(self, torch, entry, fmt, variant, M, N, K, gs, tensors, label):
+        self.entry, self.fmt, self.variant, self.M, self.N, self.K, self.gs = entry, fmt, variant, M, N, K, gs
         self.label = label
-        x, w, s, b, y = tensors
+        x, w, s, b = tensors
+        x = x[:M] if x.shape[0] != M else x
+        y = torch.empty((M, N), dtype=torch.float16, device=w.device)
+        self.t = (x, w, s, b, y)  # keep alive
         self.ptrs = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None,
                      y.data_ptr())
         self.bits = {"u1": 1, "u2": 2, "t5": 0}[fmt]
         self.bytes = algorithmic_bytes(fmt, M, N, K, gs, b is not None and entry != "bq_qmv_sym")
+
+    @property
+    def y(self):
+        return self.t[4]
 
     def launch(self, lib, stream):
         x, w, s, b, y = self.ptrs
         st = getattr(lib, self.entry)(x, w, s, b, y, self.M, self.N, self.K, self.bits, self.gs, stream)
         if st != 0:
             raise RuntimeError(f"{self.entry} {self.label}: status {st}")
+
+    def copies(self, torch, n):
+        """n calls on distinct copies of this call's inputs (copy 0 = self)."""
+        out = [self]
+        x, w, s, b, _ = self.t
+        for _ in range(n - 1):
+            ts = [t.clone() if t is not None else None for t in (x, w, s, b)]
+            out.append(Call(torch, self.entry, self.fmt, self.variant, self.M, self.N, self.K, self.gs, ts,
+                            self.label))
+        return out
 
 
 def upload(torch, a, dev):
@@ -127,25 +169,8 @@ def upload(torch, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def make_calls(torch, dev, specs, copies=None):
-    """specs: list of (entry, fmt, M, N, K, gs, variant, label).  Returns
-    calls[copy][i] with distinct device buffers per copy; by default as many
-    copies as it takes for all of them to fill COLD_BYTES."""
-    import synth
-    base = []
-    for (entry, fmt, M, N, K, gs, variant, label) in specs:
-        inp = synth.make_inputs(fmt, M, N, K, gs, variant, seed=0)
-        base.append([upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)])
-    if copies is None:
-        per_copy = sum(sum(t.numel() * t.element_size() for t in ts if t is not None) for ts in base)
-        copies = n_copies(per_copy)
-    out = [[] for _ in range(copies)]
-    for (entry, fmt, M, N, K, gs, variant, label), ts in zip(specs, base):
-        for c in range(copies):
-            x, w, s, b = [t if (c == 0 or t is None) else t.clone() for t in ts]
-            y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            out[c].append(Call(entry, fmt, M, N, K, gs, (x, w, s, b, y), label))
-    return out
+def n_copies(bytes_per_copy, cap=400):
+    return min(cap, max(2, -(-COLD_BYTES // max(1, bytes_per_copy))))
 
 
 def capture(torch, lib, calls, reps=1):
@@ -170,45 +195,111 @@ def time_graphs(torch, graphs, replays):
     return start.elapsed_time(end) * 1e-3  # seconds
 
 
-def per_call_seconds(torch, lib, call_copies, launches=40, replays=5):
-    """Average duration of one call: graph of back-to-back launches rotating
-    through the buffer copies (at least `launches`, at least one pass over
-    the copies), replayed `replays` times."""
-    launches = max(launches, len(call_copies))
-    seq = [call_copies[i % len(call_copies)] for i in range(launches)]
+def rotation_seconds(torch, lib, seq, replays=3):
+    """Average launch period of a sequence of calls on distinct buffers:
+    graph of the sequence, replayed `replays` times after one warm replay."""
     g = capture(torch, lib, seq)
     g.replay()
     t = time_graphs(torch, [g], replays)
-    return t / (launches * replays)
+    del g
+    return t / (len(seq) * replays)
 
 
-def cpu_baseline(shapes):
+def per_call_seconds(torch, lib, call, launches=40, replays=3):
+    """Average duration of one call, launched back to back on copies of its
+    inputs whose total exceeds the last-level cache (at least `launches`)."""
+    cps = call.copies(torch, n_copies(call.bytes))
+    seq = [cps[i % len(cps)] for i in range(max(launches, len(cps)))]
+    t = rotation_seconds(torch, lib, seq, replays)
+    del cps, seq
+    return t
+
+
+# --------------------------------------------------------------------------
+# The step
+# --------------------------------------------------------------------------
+def build_step(torch, dev):
+    sets = {}
+    for fmt, variant, _ in FAMILIES:
+        for gs in GROUP_SIZES:
+            for shape in SHAPES:
+                sets[(fmt, variant, gs, shape)] = WeightSet(torch, dev, fmt, variant, gs, shape)
+    calls = []
+    for M in MS:
+        for fmt, variant, entry in FAMILIES:
+            for gs in GROUP_SIZES:
+                for shape in SHAPES:
+                    ws = sets[(fmt, variant, gs, shape)]
+                    calls.append(Call(torch, entry, fmt, variant, M, ws.N, ws.K, gs, ws.dev,
+                                      f"{fmt}-{variant}/gs{gs}/M{M}/{shape}"))
+                    calls[-1].set = ws
+    return sets, calls
+
+
+def sample_rows(N, label):
+    import numpy as np
+    import synth
+    rng = np.random.default_rng(synth.seed_for("bench-rows", label))
+    return np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 3)]))
+
+
+def outputs_for_parity(torch, lib, calls):
+    """Runs every call once (eager) and keeps sampled rows of its output."""
+    h = torch.cuda.current_stream().cuda_stream
+    for c in calls:
+        c.launch(lib, h)
+    torch.cuda.synchronize()
+    out = []
+    for c in calls:
+        rows = sample_rows(c.N, c.label)
+        out.append((rows, c.y[:, torch.as_tensor(rows, device=c.y.device)].float().cpu().numpy()))
+    return out
+
+
+def cpu_baseline_leg(calls, gpu_rows, family):
+    """The CPU leg: (1) the oracle on sampled rows of every timed call,
+    compared with the outputs the same device buffers gave; (2) the oracle
+    timed on the dominant family's seven shapes (full weight matrices)."""
     import numpy as np
     import oracle
-    import synth
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = 1
+    worst, worst_label, bad = 0.0, "", []
+    for c, (rows, y) in zip(calls, gpu_rows):
+        h = c.set.host
+        y_ref, mass = oracle.qmv_reference(c.fmt, h.x[:c.M], h.w, h.scales, h.biases, c.K, c.gs, rows)
+        ok, r = oracle.check_close(y.astype(np.float64), y_ref, mass)
+        if r > worst:
+            worst, worst_label = r, c.label
+        if not ok:
+            bad.append(c.label)
+    parity = {"calls": len(calls), "rows_checked": int(sum(len(r) for r, _ in gpu_rows)),
+              "worst_err_over_tol": round(worst, 4), "worst_call": worst_label, "failed": bad,
+              "rule": "|y - y_ref| <= 1e-3*sum_k|x_k w_k| + 1e-3*|y_ref| (fp64 oracle)"}
+    fmt, variant, gs, M = family
     total_bytes, total_t = 0, 0.0
-    for shape in shapes:
-        N, K = synth.PROJECTION_SHAPES[shape]
-        inp = synth.make_inputs("u2", 1, N, K, 64, "asym", seed=0)
+    for c in calls:
+        if (c.fmt, c.variant, c.gs, c.M) != family:
+            continue
+        h = c.set.host
         t0 = time.perf_counter()
-        y, _ = oracle.qmv_reference("u2", inp.x, inp.w, inp.scales, inp.biases, K, 64)
+        y, _ = oracle.qmv_reference(fmt, h.x[:M], h.w, h.scales, h.biases, c.K, gs)
         total_t += time.perf_counter() - t0
-        total_bytes += algorithmic_bytes("u2", 1, N, K, 64, True)
+        total_bytes += c.bytes
         del y
-    return {
+    base = {
         "value": round(total_bytes / total_t / 1e9, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle (unpack, dequantize, x@W^T), 2-bit gs=64 M=1, shapes {','.join(shapes)}: "
-                  f"{total_bytes / 1e6:.1f} MB in {total_t:.2f} s; host cores visible "
-                  f"{len(os.sched_getaffinity(0))}, BLAS threads {blas_threads}",
+        "sample": f"fp64 numpy oracle (unpack, dequantize, x@W^T) on {family_key(*family[:2], gs, M)}, "
+                  f"shapes {','.join(SHAPES)}: {total_bytes / 1e6:.1f} MB in {total_t:.2f} s; host cores "
+                  f"visible {len(os.sched_getaffinity(0))}, BLAS threads {blas_threads}",
     }
+    return base, parity
 
 
 def kernel_source_hash():
@@ -222,15 +313,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
+def measured_traffic(key):
     """HBM traffic per launch from committed counter runs, if they were taken
     on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        rec = data.get(kernel_key)
+        rec = json.load(open(path)).get(key)
         if rec and rec.get("source_hash") == kernel_source_hash():
             return rec.get("bytes_per_launch")
     except Exception:  # noqa: BLE001
@@ -238,57 +328,212 @@ def measured_traffic(kernel_key):
     return None
 
 
+# --------------------------------------------------------------------------
+# Eager launch sets for counter runs
+# --------------------------------------------------------------------------
+def parse_family(key):
+    fv, g, m = key.split("/")
+    fmt, variant = fv.split("-")
+    return fmt, variant, int(g[2:]), int(m[1:])
+
+
+def launch_set_specs(name):
+    """(entry, fmt, variant, M, shape, gs) of a named eager launch set."""
+    if name.startswith("family:"):
+        fmt, variant, gs, M = parse_family(name.split(":", 1)[1])
+        return [(ENTRY_OF[(fmt, variant)], fmt, variant, M, s, gs) for s in SHAPES]
+    if name == "decode":
+        return [(ENTRY_OF[(f, v)], f, v, M, s, 64) for f, v in (("u2", "asym"), ("t5", "t5"))
+                for s in ("gate", "down") for M in MS]
+    if name == "t5":
+        return [("bq_t5_qmv_wide", "t5", "t5", M, s, gs) for gs in GROUP_SIZES for M in (1, 5) for s in SHAPES]
+    if name == "qmm":
+        return [("bq_t5_qmm", "t5", "t5", M, s, 128) for s in ("gate", "down") for M in (32, 512, 2048)]
+    if name == "dequant":
+        return [("bq_dequant", f, "asym" if f != "t5" else "t5", 0, s, 64) for f in ("u1", "u2", "t5")
+                for s in ("gate", "down")]
+    raise SystemExit(f"unknown launch set {name!r}")
+
+
+def launch_set_run(torch, lib, dev, name):
+    """One calibration copy kernel of CAL_BYTES read and CAL_BYTES written,
+    then each call of the set once, each after a pass over CAL_BYTES that
+    evicts the last-level cache, so its inputs come from HBM."""
+    import synth
+    src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    torch.add(src, 1.0, out=dst)  # calibration: reads and writes CAL_BYTES
+    torch.cuda.synchronize()
+    h = torch.cuda.current_stream().cuda_stream
+    labels, nbytes = [], []
+    for entry, fmt, variant, M, shape, gs in launch_set_specs(name):
+        N, K = synth.PROJECTION_SHAPES[shape]
+        inp = synth.make_inputs(fmt, max(M, 1), N, K, gs, variant, seed=0)
+        x, w, s, b = [upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)]
+        torch.add(dst, 1.0, out=src)  # evicts the last-level cache
+        torch.cuda.synchronize()
+        if entry == "bq_dequant":
+            y = torch.empty((N, K), dtype=torch.float16, device=dev)
+            st = lib.bq_dequant(None, w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None,
+                                y.data_ptr(), 0, N, K, inp.bits, gs, h)
+            nb = w.numel() * w.element_size() + s.numel() * 2 * (2 if b is not None else 1) + N * K * 2
+        else:
+            c = Call(torch, entry, fmt, variant, M, N, K, gs, (x, w, s, b), "")
+            st = 0
+            c.launch(lib, h)
+            nb = c.bytes
+        if st != 0:
+            raise RuntimeError(f"{entry}: status {st}")
+        torch.cuda.synchronize()
+        labels.append(f"{entry}/{fmt}-{variant}/gs{gs}/M{M}/{shape}")
+        nbytes.append(nb)
+        del x, w, s, b
+    print(json.dumps({"launch_set": name, "calls": labels, "bytes": nbytes}), flush=True)
+
+
+def traffic_from(fetch_csv, write_csv, key):
+    """profiles/traffic.json entry for family KEY from the counter_collection
+    CSVs of two --launch-set family:KEY runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch)."""
+    import csv
+
+    import synth
+    fmt, variant, gs, M = parse_family(key)
+
+    def read(path, counter):
+        rows = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return rows
+
+    out, per = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = read(path, counter)
+        cal = [v for (_, name, v) in rows if "elementwise" in name and "_add" in name]
+        qmv = [v for (_, name, v) in rows if "qmv_kernel" in name]
+        if not cal or len(qmv) != len(SHAPES):
+            raise SystemExit(f"{path}: expected a calibration copy and {len(SHAPES)} qmv dispatches, "
+                             f"found {len(cal)} and {len(qmv)}")
+        factor = cal[0] * 1024.0 / CAL_BYTES  # counter KiB per true KiB
+        per[counter] = [v * 1024.0 / factor for v in qmv]
+        out[counter] = {"calibration_kib": cal[0], "factor": round(factor, 4),
+                        "kib_per_dispatch": [round(v, 1) for v in qmv]}
+    per_launch = [f + w for f, w in zip(per["FETCH_SIZE"], per["WRITE_SIZE"])]
+    stored = variant == "asym"
+    alg = [algorithmic_bytes(fmt, M, *synth.PROJECTION_SHAPES[s], gs, stored) for s in SHAPES]
+    rec = {
+        "source_hash": kernel_source_hash(),
+        "shapes": list(SHAPES),
+        "bytes_per_launch": int(sum(per_launch) / len(per_launch)),
+        "algorithmic_bytes_per_launch": int(sum(alg) / len(alg)),
+        "per_shape_bytes": [int(v) for v in per_launch],
+        "per_shape_algorithmic_bytes": alg,
+        "counters": out,
+        "method": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, on python3 bench.py --launch-set family:"
+                  f"{key}; each divided by what it reads for a copy of {CAL_BYTES >> 20} MiB read + "
+                  f"{CAL_BYTES >> 20} MiB written",
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[key] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
+# --------------------------------------------------------------------------
+# Full suite (CSV)
+# --------------------------------------------------------------------------
 def full_suite(torch, lib, dev, path):
     import synth
-    rows = []
     specs = []
-    for fmt in ("u1", "u2"):
-        for gs in (64, 128):
-            for M in (1, 2, 3, 4, 5):
-                for variant, entry in (("asym", "bq_qmv_wide"), ("sym", "bq_qmv_sym")):
+    for M in MS:
+        for fmt in ("u1", "u2"):
+            for gs in GROUP_SIZES:
+                for variant in ("asym", "sym"):
                     for shape in SHAPES:
-                        N, K = synth.PROJECTION_SHAPES[shape]
-                        specs.append((entry, fmt, M, N, K, gs, variant, shape))
+                        specs.append((ENTRY_OF[(fmt, variant)], fmt, variant, M, shape, gs))
                 for shape in ("gate", "down"):  # W read M times
-                    N, K = synth.PROJECTION_SHAPES[shape]
-                    specs.append(("bq_qmv", fmt, M, N, K, gs, "asym", shape))
-    for gs in (64, 128):
-        for M in (1, 2, 3, 4, 5):
+                    specs.append(("bq_qmv", fmt, "asym", M, shape, gs))
+        for gs in GROUP_SIZES:
             for shape in SHAPES:
-                N, K = synth.PROJECTION_SHAPES[shape]
-                specs.append(("bq_t5_qmv_wide", "t5", M, N, K, gs, "t5", shape))
-    qmm_specs = []
+                specs.append(("bq_t5_qmv_wide", "t5", "t5", M, shape, gs))
     for M in (32, 512, 2048):
         for shape in ("gate", "down"):
-            N, K = synth.PROJECTION_SHAPES[shape]
-            qmm_specs.append(("bq_t5_qmm", "t5", M, N, K, 128, "t5", shape))
+            specs.append(("bq_t5_qmm", "t5", "t5", M, shape, 128))
             for fmt in ("u1", "u2"):
-                qmm_specs.append(("bq_qmm", fmt, M, N, K, 128, "asym", shape))
+                specs.append(("bq_qmm", fmt, "asym", M, shape, 128))
+    rows = []
     with open(path, "w") as f:
         f.write("entry,fmt,variant,M,shape,N,K,gs,us,GBps,frac_hbm,TFLOPs\n")
-        for spec in specs + qmm_specs:
-            copies = make_calls(torch, dev, [spec])
-            pair = [cs[0] for cs in copies]
-            mm = spec[0] in ("bq_t5_qmm", "bq_qmm")
-            launches = 8 if mm and spec[2] >= 512 else 40
-            t = per_call_seconds(torch, lib, pair, launches=launches, replays=3)
-            c = pair[0]
+        for entry, fmt, variant, M, shape, gs in specs:
+            N, K = synth.PROJECTION_SHAPES[shape]
+            inp = synth.make_inputs(fmt, M, N, K, gs, variant, seed=0)
+            c = Call(torch, entry, fmt, variant, M, N, K, gs,
+                     [upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)], "")
+            mm = entry in ("bq_t5_qmm", "bq_qmm")
+            t = per_call_seconds(torch, lib, c, launches=8 if mm and M >= 512 else 40, replays=3)
             gbs = c.bytes / t / 1e9
-            tflops = (2.0 * c.M * c.N * c.K / t / 1e12) if mm else 0.0
-            line = (f"{spec[0]},{spec[1]},{spec[6]},{spec[2]},{spec[7]},{spec[3]},{spec[4]},{spec[5]},"
-                    f"{t * 1e6:.3f},{gbs:.1f},{gbs / PEAK_HBM_GBS:.4f},{tflops:.1f}")
+            tflops = (2.0 * M * N * K / t / 1e12) if mm else 0.0
+            line = (f"{entry},{fmt},{variant},{M},{shape},{N},{K},{gs},{t * 1e6:.3f},{gbs:.1f},"
+                    f"{gbs / PEAK_HBM_GBS:.4f},{tflops:.1f}")
             f.write(line + "\n")
             f.flush()
             print(line, file=sys.stderr, flush=True)
             rows.append(line)
-            del copies, pair
+            del c
             torch.cuda.empty_cache()
-        for line in spec_and_repack_rows(torch, lib, dev):
+        for line in dequant_rows(torch, lib, dev) + spec_and_repack_rows(torch, lib, dev):
             f.write(line + "\n")
             f.flush()
             print(line, file=sys.stderr, flush=True)
             rows.append(line)
     return rows
+
+
+def dequant_rows(torch, lib, dev):
+    """bq_dequant for bits 1, 2 and t5 (gs 64 and 128, stored and implied
+    biases) on gate and down: bytes = packed W + scales (+ biases) read +
+    N*K*2 written; graph of back-to-back launches over rotating inputs and
+    two outputs."""
+    import synth
+    out = []
+    h = torch.cuda.current_stream().cuda_stream
+    for fmt in ("u1", "u2", "t5"):
+        for gs in GROUP_SIZES:
+            for variant in (("asym", "sym") if fmt != "t5" else ("t5", "asym")):
+                for shape in ("gate", "down"):
+                    N, K = synth.PROJECTION_SHAPES[shape]
+                    inp = synth.make_inputs(fmt, 1, N, K, gs, variant, seed=0)
+                    ins = [[upload(torch, a, dev) for a in (inp.w, inp.scales, inp.biases)]]
+                    ins += [[t.clone() if t is not None else None for t in ins[0]] for _ in range(3)]
+                    ys = [torch.empty((N, K), dtype=torch.float16, device=dev) for _ in range(2)]
+                    bits = inp.bits
+                    g = torch.cuda.CUDAGraph()
+                    n = 8
+                    with torch.cuda.graph(g):
+                        hs = torch.cuda.current_stream().cuda_stream
+                        for i in range(n):
+                            w, s, b = ins[i % len(ins)]
+                            st = lib.bq_dequant(None, w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None
+                                                else None, ys[i % 2].data_ptr(), 0, N, K, bits, gs, hs)
+                            if st != 0:
+                                raise RuntimeError(f"bq_dequant: status {st}")
+                    g.replay()
+                    t = time_graphs(torch, [g], 3) / (3 * n)
+                    w, s, b = ins[0]
+                    nb = w.numel() * w.element_size() + s.numel() * 2 * (2 if b is not None else 1) + N * K * 2
+                    gbs = nb / t / 1e9
+                    out.append(f"bq_dequant,{fmt},{variant},0,{shape},{N},{K},{gs},{t * 1e6:.3f},{gbs:.1f},"
+                               f"{gbs / PEAK_HBM_GBS:.4f},0.0")
+                    del g, ins, ys
+                    torch.cuda.empty_cache()
+    del h
+    return out
 
 
 def spec_and_repack_rows(torch, lib, dev):
@@ -344,108 +589,13 @@ def spec_and_repack_rows(torch, lib, dev):
     return out
 
 
-def counter_run(torch, lib, dev):
-    """Eager launches for counter runs: one calibration copy kernel of
-    CAL_BYTES read and CAL_BYTES written, then each shape of the dominant
-    kernel once, each after a fresh pass of the calibration copy so that its
-    inputs come from HBM."""
-    import synth
-    src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
-    dst = torch.empty_like(src)
-    torch.add(src, 1.0, out=dst)  # calibration: reads and writes CAL_BYTES
-    torch.cuda.synchronize()
-    specs = []
-    for shape in SHAPES:
-        N, K = synth.PROJECTION_SHAPES[shape]
-        specs.append(("bq_qmv", "u2", 1, N, K, 64, "asym", f"u2/gs64/{shape}"))
-    calls = make_calls(torch, dev, specs, copies=1)[0]
-    h = torch.cuda.current_stream().cuda_stream
-    for c in calls:
-        torch.add(dst, 1.0, out=src)  # evicts the last-level cache
-        torch.cuda.synchronize()
-        c.launch(lib, h)
-        torch.cuda.synchronize()
-    print(json.dumps({"counter_run": [c.label for c in calls], "bytes": [c.bytes for c in calls]}), flush=True)
-
-
-def qmm_counter_run(torch, lib, dev):
-    """Eager launches for matrix-core counter runs: t5_qmm (gs 128) on the
-    gate and down shapes at M = 32, 512, 2048, each after a pass over
-    CAL_BYTES that evicts the last-level cache."""
-    import synth
-    src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
-    dst = torch.empty_like(src)
-    specs = []
-    for shape in ("gate", "down"):
-        N, K = synth.PROJECTION_SHAPES[shape]
-        for M in (32, 512, 2048):
-            specs.append(("bq_t5_qmm", "t5", M, N, K, 128, "t5", f"t5_qmm/gs128/{shape}/M{M}"))
-    calls = make_calls(torch, dev, specs, copies=1)[0]
-    h = torch.cuda.current_stream().cuda_stream
-    for c in calls:
-        torch.add(src, 1.0, out=dst)  # evicts the last-level cache
-        torch.cuda.synchronize()
-        c.launch(lib, h)
-        torch.cuda.synchronize()
-    print(json.dumps({"qmm_counter_run": [c.label for c in calls],
-                      "flops": [2 * c.M * c.N * c.K for c in calls]}), flush=True)
-
-
-def traffic_from(fetch_csv, write_csv):
-    """profiles/traffic.json from the counter_collection.csv files of two
-    --counters runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)."""
-    import csv
-
-    def read(path, counter):
-        rows = []
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
-                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
-        rows.sort()
-        return rows
-
-    out = {}
-    per = {}
-    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        rows = read(path, counter)
-        # the calibration copy: the first elementwise add (not the fill that made its input)
-        cal = [v for (_, name, v) in rows if "elementwise" in name and "_add" in name]
-        qmv = [v for (_, name, v) in rows if "qmv_kernel<2, 64, 1, false" in name]
-        if not cal or len(qmv) != len(SHAPES):
-            raise SystemExit(f"{path}: expected a calibration copy and {len(SHAPES)} qmv dispatches, "
-                             f"found {len(cal)} and {len(qmv)}")
-        factor = cal[0] * 1024.0 / CAL_BYTES  # counter KiB per true KiB
-        per[counter] = [v * 1024.0 / factor for v in qmv]
-        out[counter] = {"calibration_kib": cal[0], "factor": round(factor, 4),
-                        "kib_per_dispatch": [round(v, 1) for v in qmv]}
-    per_launch = [f + w for f, w in zip(per["FETCH_SIZE"], per["WRITE_SIZE"])]
-    import synth
-    alg = [algorithmic_bytes("u2", 1, *synth.PROJECTION_SHAPES[s], 64, True) for s in SHAPES]
-    rec = {
-        "source_hash": kernel_source_hash(),
-        "shapes": list(SHAPES),
-        "bytes_per_launch": int(sum(per_launch) / len(per_launch)),
-        "algorithmic_bytes_per_launch": int(sum(alg) / len(alg)),
-        "per_shape_bytes": [int(v) for v in per_launch],
-        "per_shape_algorithmic_bytes": alg,
-        "counters": out,
-        "method": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, on python3 bench.py --counters; each divided "
-                  f"by what it reads for a copy of {CAL_BYTES >> 20} MiB read + {CAL_BYTES >> 20} MiB written",
-    }
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    data = json.load(open(path)) if os.path.exists(path) else {}
-    data[DOMINANT] = rec
-    with open(path, "w") as f:
-        json.dump(data, f, indent=1)
-        f.write("\n")
-    print(json.dumps(rec), flush=True)
-
-
+# --------------------------------------------------------------------------
 def main():
     args = parse()
     if args.traffic_from:
-        traffic_from(*args.traffic_from)
+        if not args.family:
+            raise SystemExit("--traffic-from needs --family KEY")
+        traffic_from(*args.traffic_from, args.family)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -456,7 +606,6 @@ def main():
     import torch
 
     import bit_quantized_decode_qmv_amd as bq
-    import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -464,39 +613,27 @@ def main():
     lib = bq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.counters:
-        counter_run(torch, lib, dev)
-        return
-    if args.qmm_counters:
-        qmm_counter_run(torch, lib, dev)
+    if args.launch_set:
+        launch_set_run(torch, lib, dev, args.launch_set)
         return
 
-    specs = []
-    for bits in (1, 2):
-        fmt = "u1" if bits == 1 else "u2"
-        for gs in (64, 128):
-            for shape in SHAPES:
-                N, K = synth.PROJECTION_SHAPES[shape]
-                specs.append(("bq_qmv", fmt, 1, N, K, gs, "asym", f"{fmt}/gs{gs}/{shape}"))
-    copies = make_calls(torch, dev, specs)
-    print(f"bench: {len(specs)} calls x {len(copies)} copies", file=sys.stderr, flush=True)
-    step_bytes = sum(c.bytes for c in copies[0])
+    sets, calls = build_step(torch, dev)
+    step_bytes = sum(c.bytes for c in calls)
+    print(f"bench: {len(calls)} calls per step, {step_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
 
-    # eager warm-up (loads the code object before any capture)
-    h = torch.cuda.current_stream().cuda_stream
-    for cs in copies:
-        for c in cs:
-            c.launch(lib, h)
-    torch.cuda.synchronize()
+    # eager pass: loads the code objects before any capture, and leaves the
+    # outputs whose sampled rows the CPU leg checks against the oracle
+    gpu_rows = outputs_for_parity(torch, lib, calls)
 
-    graphs = [capture(torch, lib, cs) for cs in copies]
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+    graph = capture(torch, lib, calls)
+    for _ in range(args.warmup):
+        graph.replay()
     torch.cuda.synchronize()
     print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
-    elapsed = time_graphs(torch, graphs, args.steps)
+    elapsed = time_graphs(torch, [graph], args.steps)
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes * args.steps / elapsed / 1e9
+    del graph
 
     result = {
         "metric": METRIC,
@@ -512,57 +649,77 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "decode QMV M=1, 7 projection shapes of a hidden=5120 decoder, bits {1,2} x "
-                        "group_size {64,128}, affine (stored biases)",
-            "M": 1,
-            "calls_per_step": len(specs),
+            "workload": "decode QMV of one hidden=5120 decoder layer: 7 projection shapes x M=1..5 x {2-bit "
+                        "affine (bq_qmv_wide), 2-bit symmetric (bq_qmv_sym), t5 ternary (bq_t5_qmv_wide)} x "
+                        "group_size {64,128}",
+            "M": list(MS),
+            "calls_per_step": len(calls),
             "bytes_per_step": step_bytes,
             "parallelism": "single GPU",
         },
     }
 
     if not args.profile_only:
-        # dominant kernel: 2-bit, gs=64, M=1 affine, over its seven shapes
-        dom_specs = [sp for sp in specs if sp[1] == "u2" and sp[5] == 64]
-        dom_copies = make_calls(torch, dev, dom_specs)
-        seq = [c for cs in dom_copies for c in cs]
-        gd = capture(torch, lib, seq)
-        gd.replay()
-        reps = 5
-        t = time_graphs(torch, [gd], reps)
-        avg_launch = t / (reps * len(seq))
-        bytes_per_launch = sum(c.bytes for c in dom_copies[0]) / len(dom_copies[0])
+        # per-call durations, each call alone over rotating copies of its inputs
+        per = {}
+        if not args.no_breakdown:
+            print("bench: per-call breakdown", file=sys.stderr, flush=True)
+            for c in calls:
+                per[c.label] = per_call_seconds(torch, lib, c, launches=20, replays=3)
+                torch.cuda.empty_cache()
+            result["breakdown"] = {k: {"us": round(v * 1e6, 2),
+                                       "GBps": round(next(c.bytes for c in calls if c.label == k) / v / 1e9, 1)}
+                                   for k, v in per.items()}
+        fam_t = {}
+        for c in calls:
+            k = (c.fmt, c.variant, c.gs, c.M)
+            fam_t[k] = fam_t.get(k, 0.0) + per.get(c.label, 0.0)
+        tot = sum(fam_t.values()) or 1.0
+        if per:
+            result["families"] = {family_key(*k[:2], k[2], k[3]): {"us": round(v * 1e6, 2),
+                                                                    "share": round(v / tot, 4)}
+                                  for k, v in sorted(fam_t.items(), key=lambda kv: -kv[1])}
+            dom = max(fam_t, key=fam_t.get)
+        else:
+            dom = ("t5", "t5", 64, 5)
+        fmt, variant, gs, M = dom
+        key = family_key(fmt, variant, gs, M)
+        # roofline of the dominant family: its seven launches, rotating copies
+        fam_calls = [c for c in calls if (c.fmt, c.variant, c.gs, c.M) == dom]
+        per_copy = sum(c.bytes for c in fam_calls)
+        ncp = n_copies(per_copy, cap=64)
+        copies = [c.copies(torch, ncp) for c in fam_calls]
+        seq = [copies[i][j] for j in range(ncp) for i in range(len(fam_calls))]
+        avg_launch = rotation_seconds(torch, lib, seq, replays=5)
+        bytes_per_launch = per_copy / len(fam_calls)
         achieved = bytes_per_launch / avg_launch / 1e9
-        del gd, dom_copies, seq
+        del copies, seq
+        torch.cuda.empty_cache()
         result["roofline"] = {
             "bound": "hbm",
-            "kernel": "qmv_kernel<2-bit, gs=64, M=1, stored bias>",
+            "kernel": f"qmv_kernel family {key} (format-variant / group size / M) over its 7 shapes",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(DOMINANT),
+            "traffic": measured_traffic(key),
             "avg_launch_us": round(avg_launch * 1e6, 3),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "share_of_step": round(fam_t.get(dom, 0.0) / tot, 4) if per else None,
         }
-        bd = {}
-        for spec in specs:
-            cc = make_calls(torch, dev, [spec])
-            ts = per_call_seconds(torch, lib, [cs[0] for cs in cc], launches=20, replays=3)
-            c = cc[0][0]
-            bd[c.label] = {"us": round(ts * 1e6, 2), "GBps": round(c.bytes / ts / 1e9, 1)}
-            del cc
-        result["breakdown"] = bd
         if args.suite == "full":
             os.makedirs(os.path.dirname(args.detail_csv), exist_ok=True)
-            del graphs
-            torch.cuda.empty_cache()
             full_suite(torch, lib, dev, args.detail_csv)
         if not args.no_cpu_baseline:
-            shapes = [s for s in args.cpu_sample.split(",") if s]
-            print(f"bench: cpu oracle on {shapes}", file=sys.stderr, flush=True)
-            result["cpu_baseline"] = cpu_baseline(shapes)
+            print(f"bench: cpu leg (parity of {len(calls)} calls, oracle timing on {key})", file=sys.stderr,
+                  flush=True)
+            base, parity = cpu_baseline_leg(calls, gpu_rows, dom)
+            result["cpu_baseline"] = base
+            result["parity"] = parity
     print(json.dumps(result), flush=True)
+    if "parity" in result and result["parity"]["failed"]:
+        print(f"bench: parity failed for {result['parity']['failed']}", file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 if __name__ == "__main__":
