@@ -23,7 +23,7 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
@@ -41,12 +41,13 @@ LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
                 "bq_t5_qmm", "bq_dequant", "bq_qmm")
 DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack", "bq_spec_verify_workspace",
-                   "bq_spec_decode_verify")
+                   "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc")
 ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
 
 STATUS = {
     0: "BQ_OK", -1: "BQ_ERR_NULL", -2: "BQ_ERR_BITS", -3: "BQ_ERR_GROUP", -4: "BQ_ERR_SHAPE",
     -5: "BQ_ERR_M", -6: "BQ_ERR_ALIGN", -7: "BQ_ERR_HIP", -8: "BQ_ERR_FLAGS", -9: "BQ_ERR_WORKSPACE",
+    -10: "BQ_ERR_SCRATCH",
 }
 
 
@@ -90,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bq_spec_verify_workspace.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.bq_spec_decode_verify.restype = ctypes.c_int
     lib.bq_spec_decode_verify.argtypes = [vp, i, vp, i, i, i, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bq_spec_decode_verify_noalloc.restype = ctypes.c_int
+    lib.bq_spec_decode_verify_noalloc.argtypes = [vp, i, vp, i, i, i, vp, vp, vp, vp]
     ver = lib.bq_abi_version()
     if ver != ABI_VERSION:
         raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
@@ -175,6 +178,16 @@ def bq_spec_decode_verify(logits, logits_dtype, draft, B, L, V, accepted, next_t
     return _raise_if(load_library().bq_spec_decode_verify(logits, logits_dtype, draft, B, L, V, accepted, next_token,
                                                           target_tokens, workspace, workspace_bytes, stream),
                      "bq_spec_decode_verify")
+
+
+def bq_spec_decode_verify_noalloc(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens,
+                                  stream=None):
+    """C entry point bq_spec_decode_verify_noalloc of include/bq.h (pointers as
+    integers): the verify call without a workspace (static scratch inside
+    the library; no allocation)."""
+    return _raise_if(load_library().bq_spec_decode_verify_noalloc(logits, logits_dtype, draft, B, L, V, accepted,
+                                                                  next_token, target_tokens, stream),
+                     "bq_spec_decode_verify_noalloc")
 
 
 # ---------------------------------------------------------------------------
@@ -416,6 +429,7 @@ __all__ = [
     "LINEAR_SYM", "MAX_WIDE_M", "QMM_MIN_M", "QMM_MIN_TILES", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
     "bq_linear", "bq_linear_route", "bq_qmm", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
     "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmm", "qmv", "qmv_sym", "qmv_wide",
-    "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_verify_workspace",
+    "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc",
+    "bq_spec_verify_workspace",
     "bq_t5_repack", "spec_decode_verify", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
 ]

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "bq.h"
@@ -71,6 +72,35 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
 // spec verify workspace: row keys, then per-sequence counters
 size_t spec_keys_bytes(int B, int L) { return ((size_t)B * (L + 1) * 8 + 255) / 256 * 256; }
 size_t spec_workspace_bytes(int B, int L) { return spec_keys_bytes(B, L) + (size_t)B * 4; }
+
+// Scratch of the allocation-free verify entry point: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// passes its name to a kernel (on the host the name is only a stand-in):
+// it takes the device address from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = BQ_SPEC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BQ_OK;
+}
+
+// zeroes n bytes (a multiple of 4) of device memory with vector stores
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
 
 int launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* stream, void* params) {
   return launch_kernel(fn, grid, block, shmem, stream, params);
@@ -163,6 +193,40 @@ int launch_qmm(const void* x, const void* w, const void* scales, const void* bia
   return launch_qmm_u2(p, group_size, implied, stream);
 }
 
+// checks of bq_spec_decode_verify's arguments other than the workspace
+int spec_validate(const void* logits, int logits_dtype, const int* draft, int B, int L, int V, const int* accepted,
+                  const int* next_token, const int* target_tokens) {
+  if (!logits || (L > 0 && !draft) || !accepted || !next_token) return BQ_ERR_NULL;
+  if (logits_dtype != BQ_DTYPE_F16 && logits_dtype != BQ_DTYPE_F32) return BQ_ERR_BITS;
+  if (B < 1 || L < 0 || L > BQ_SPEC_MAX_DRAFT || V < 1) return BQ_ERR_SHAPE;
+  const int64_t chunks = (V + kSpecChunk - 1) / kSpecChunk;
+  if ((int64_t)B * (L + 1) * chunks >= (1ll << 31)) return BQ_ERR_SHAPE;
+  const size_t esz = logits_dtype == BQ_DTYPE_F16 ? 2 : 4;
+  if (!aligned(logits, esz) || (draft && !aligned(draft, 4)) || !aligned(accepted, 4) || !aligned(next_token, 4) ||
+      (target_tokens && !aligned(target_tokens, 4)))
+    return BQ_ERR_ALIGN;
+  return BQ_OK;
+}
+
+int spec_launch(const void* logits, int logits_dtype, const int* draft, int B, int L, int V, int* accepted,
+                int* next_token, int* target_tokens, void* workspace, void* stream) {
+  SpecParams p{};
+  p.logits = logits;
+  p.draft = draft;
+  p.accepted = accepted;
+  p.next_token = next_token;
+  p.target = target_tokens;
+  p.keys = static_cast<unsigned long long*>(workspace);
+  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + spec_keys_bytes(B, L));
+  p.B = B;
+  p.L = L;
+  p.V = V;
+  p.chunks = (int)((V + kSpecChunk - 1) / kSpecChunk);
+  const void* fn = logits_dtype == BQ_DTYPE_F16 ? reinterpret_cast<const void*>(&spec_verify_kernel<_Float16>)
+                                                : reinterpret_cast<const void*>(&spec_verify_kernel<float>);
+  return launch(fn, dim3((unsigned)((int64_t)B * (L + 1) * p.chunks)), dim3(kSpecThreads), 0, stream, &p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +249,9 @@ const char* bq_strerror(int status) {
     case BQ_ERR_FLAGS: return "flags holds bits this entry point does not define";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case BQ_ERR_WORKSPACE: return "the workspace is NULL or smaller than bq_spec_verify_workspace reports";
+    case BQ_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point's static array "
+             "(BQ_SPEC_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "unknown bq status";
 }
@@ -367,31 +434,33 @@ int bq_spec_verify_workspace(int B, int L, int V, size_t* bytes) {
 int bq_spec_decode_verify(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
                           int* accepted, int* next_token, int* target_tokens, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  if (!logits || (L > 0 && !draft) || !accepted || !next_token) return BQ_ERR_NULL;
-  if (logits_dtype != BQ_DTYPE_F16 && logits_dtype != BQ_DTYPE_F32) return BQ_ERR_BITS;
-  if (B < 1 || L < 0 || L > BQ_SPEC_MAX_DRAFT || V < 1) return BQ_ERR_SHAPE;
-  const int64_t chunks = (V + kSpecChunk - 1) / kSpecChunk;
-  if ((int64_t)B * (L + 1) * chunks >= (1ll << 31)) return BQ_ERR_SHAPE;
+  int st = spec_validate(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens);
+  if (st != BQ_OK) return st;
   if (!workspace || workspace_bytes < spec_workspace_bytes(B, L)) return BQ_ERR_WORKSPACE;
-  const size_t esz = logits_dtype == BQ_DTYPE_F16 ? 2 : 4;
-  if (!aligned(logits, esz) || (draft && !aligned(draft, 4)) || !aligned(accepted, 4) ||
-      !aligned(next_token, 4) || (target_tokens && !aligned(target_tokens, 4)) || !aligned(workspace, 8))
-    return BQ_ERR_ALIGN;
-  SpecParams p{};
-  p.logits = logits;
-  p.draft = draft;
-  p.accepted = accepted;
-  p.next_token = next_token;
-  p.target = target_tokens;
-  p.keys = static_cast<unsigned long long*>(workspace);
-  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + spec_keys_bytes(B, L));
-  p.B = B;
-  p.L = L;
-  p.V = V;
-  p.chunks = (int)chunks;
-  const void* fn = logits_dtype == BQ_DTYPE_F16 ? reinterpret_cast<const void*>(&spec_verify_kernel<_Float16>)
-                                                : reinterpret_cast<const void*>(&spec_verify_kernel<float>);
-  return launch(fn, dim3((unsigned)((int64_t)B * (L + 1) * chunks)), dim3(kSpecThreads), 0, stream, &p);
+  if (!aligned(workspace, 8)) return BQ_ERR_ALIGN;
+  return spec_launch(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens, workspace, stream);
+}
+
+int bq_spec_decode_verify_noalloc(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
+                                  int* accepted, int* next_token, int* target_tokens, void* stream) {
+  int st = spec_validate(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens);
+  if (st != BQ_OK) return st;
+  const size_t need = spec_workspace_bytes(B, L);
+  if (need > kScratchBytes) return BQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BQ_OK) return st;
+  // the verify kernel needs its keys and counters zero; the array keeps the
+  // last call's contents, so they are cleared first (a kernel, not a
+  // memset: graph-capture safe)
+  const size_t words = (need + 3) / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 256);
+  size_t nw = words;
+  void* args[] = {&ws, &nw};
+  if (hipLaunchKernel(reinterpret_cast<const void*>(&zero_fill_kernel), dim3(blocks), dim3(256), args, 0,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return BQ_ERR_HIP;
+  return spec_launch(logits, logits_dtype, draft, B, L, V, accepted, next_token, target_tokens, ws, stream);
 }
 
 }  // extern "C"

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 6
+#define BQ_ABI_VERSION 7
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -78,7 +78,9 @@ typedef enum bq_status {
   BQ_ERR_ALIGN = -6,      /* a pointer is misaligned, or a t5 repack with K % 256 != 0 */
   BQ_ERR_HIP = -7,        /* the HIP runtime rejected a launch */
   BQ_ERR_FLAGS = -8,      /* bq_linear: flags holds undefined bits */
-  BQ_ERR_WORKSPACE = -9   /* bq_spec_decode_verify: workspace NULL or too small */
+  BQ_ERR_WORKSPACE = -9,  /* bq_spec_decode_verify: workspace NULL or too small */
+  BQ_ERR_SCRATCH = -10    /* bq_spec_decode_verify_noalloc: the call needs more than
+                             BQ_SPEC_NOALLOC_SCRATCH_BYTES of scratch */
 } bq_status;
 
 /* bq_linear flags */
@@ -241,6 +243,24 @@ int bq_spec_verify_workspace(int B, int L, int V, size_t* bytes);
 int bq_spec_decode_verify(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
                           int* accepted, int* next_token, int* target_tokens, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* bq_spec_decode_verify for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without a workspace.  Its
+ * scratch is a static device array of BQ_SPEC_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, held until the process ends; the call clears
+ * what it uses (a kernel, no memset), then runs the verify kernel: two
+ * launches, no allocation of any kind.  A call whose scratch,
+ * bq_spec_verify_workspace(B, L), exceeds the array returns BQ_ERR_SCRATCH
+ * before launching anything (e.g. B = 256 sequences of L = 15 draft tokens
+ * need about 33 KB).  Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (several streams, several host threads)
+ * race and give wrong results; serialize them.  Other errors as
+ * bq_spec_decode_verify; BQ_ERR_HIP if the array's address cannot be
+ * taken. */
+#define BQ_SPEC_NOALLOC_SCRATCH_BYTES (256 * 1024)
+int bq_spec_decode_verify_noalloc(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
+                                  int* accepted, int* next_token, int* target_tokens, void* stream);
 
 #ifdef __cplusplus
 }

@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 6
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 7
 
 
 def test_strerror_covers_every_status(lib):
@@ -360,3 +360,34 @@ def test_spec_verify_validates(lib):
     assert sv(n=A + 66) == ALIGN
     assert sv(t=T + 2) == ALIGN
     assert sv(w=W + 4) == ALIGN
+
+
+SCRATCH_ERR = -10
+
+
+def test_spec_verify_noalloc_validates(lib):
+    """The allocation-free verify call checks the same arguments and refuses,
+    before any launch, a call whose scratch exceeds its static array."""
+    import ctypes
+    D, A, T = PX, PW, PS
+
+    def sv(lg=PY, dt=1, d=D, B=2, L=3, V=1000, a=A, n=A + 64, t=T):
+        return lib.bq_spec_decode_verify_noalloc(lg, dt, d, B, L, V, a, n, t, None)
+    assert sv(lg=None) == NULL
+    assert sv(d=None) == NULL
+    assert sv(a=None) == NULL
+    assert sv(n=None) == NULL
+    for dt in (0, 3):
+        assert sv(dt=dt) == BITS
+    assert sv(B=0) == SHAPE
+    assert sv(L=1025) == SHAPE
+    assert sv(lg=PY + 1) == ALIGN
+    assert sv(t=T + 2) == ALIGN
+    # scratch: keys of B*(L+1) rows (rounded to 256 bytes) + B counters
+    limit = 256 * 1024
+    n = ctypes.c_size_t(0)
+    assert lib.bq_spec_verify_workspace(4096, 15, 1000, ctypes.byref(n)) == OK and n.value > limit
+    assert sv(B=4096, L=15) == SCRATCH_ERR
+    assert lib.bq_spec_verify_workspace(256, 15, 1000, ctypes.byref(n)) == OK and n.value <= limit
+    assert bq.STATUS[SCRATCH_ERR] == "BQ_ERR_SCRATCH"
+    assert "scratch" in bq.strerror(SCRATCH_ERR)
