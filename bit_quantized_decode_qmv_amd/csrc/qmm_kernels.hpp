@@ -21,16 +21,22 @@
 //   eight 16-byte units, stored at unit (q XOR row%8) so that the MFMA
 //   operand reads of 16 rows hit distinct banks.
 // * Weights: each decoding thread takes BN/4 codes of one weight row per
-//   step.  Their t5 bytes (at most 14) are loaded one step ahead as a
-//   16-byte window and realigned; a 256-entry LDS table gives each byte's five digits
-//   as 6-bit fields holding 16*digit, which is the shift that picks the
-//   code's fp16 weight out of the row's three possible weights held in one
-//   64-bit register: {-s, 0, s} when the bias is -scale (exact), otherwise
-//   the correctly rounded s*q + b for q = 0, 1, 2.  Two codes then cost one
-//   bit-field extract and one 64-bit shift each plus one pack.
+//   step.  Their t5 bytes (at most 14) are loaded ahead as a 16-byte window
+//   from the dword at or below the first byte and realigned with
+//   v_alignbyte.  An LDS table gives, for each byte value and each pair of
+//   its five digits, a v_perm_b32 selector that picks the pair's two fp16
+//   weights out of the row's three possible weights (held in two dwords:
+//   {-s, 0, s} when the bias is -scale, exact, otherwise the correctly
+//   rounded s*q + b for q = 0, 1, 2), so two codes cost one v_perm.  The
+//   uint32 decoder does the same with a table of selectors per byte of
+//   four 2-bit or eight 1-bit codes.
 // * Per step: the multiplying waves work on one buffer while the others fill
 //   the second one (x loads, weight decode, and the byte and scale loads of
 //   the step after); then one barrier.
+// * Small M (32-row tiles), where an iteration is far shorter than a memory
+//   round trip: a variant requests x and the raw bytes several iterations
+//   ahead into register sets, with the two kinds of waves in loops of their
+//   own (see qmm_deep_kernel).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -500,6 +506,220 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   if (producer) return;
 
   // D layout of 16x16x32: lane holds rows 4*(lane/16)+v, column lane%16
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + v;
+        const int n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
+        if (m < p.M && n < p.N) p.y[(size_t)m * p.N + n] = (half_t)acc[i][j][v];
+      }
+}
+
+
+// ---------------------------------------------------------------------------
+// The product for small M (32-row tiles), where one K iteration of a tile is
+// far shorter than a memory round trip.  Same work split and LDS layout as
+// qmm_kernel, but the loading waves request x and the raw weight bytes D
+// iterations ahead, into D register sets, and store an iteration's x to LDS
+// (next to its decoded weights) one iteration before it is multiplied.  An
+// iteration then waits only for loads issued D - 1 iterations earlier.
+//
+// The two kinds of waves run separate loops with the same barriers: the
+// compiler places the waits for loaded registers from the loads it sees on
+// each path, and a loop shared by both kinds would merge the loading
+// waves' state with that of waves that never load, which makes every
+// register set look freshly requested (a wait for all loads in flight).
+// The products and their order are those of qmm_kernel, so the output is
+// the same bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void keep_loaded(const u32x4& d) { asm volatile("" ::"v"(d)); }
+template <int N>
+__device__ __forceinline__ void keep_loaded(const uint32_t (&d)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(d[i]));
+}
+
+constexpr size_t qmm_deep_lds_bytes(int BM, int BN, int lut_words, int SUB) { return qmm_lds_bytes(BM, BN, lut_words, SUB); }
+
+template <int BM, int BN, class Dec, int SUB, int D>
+__global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
+  constexpr int MB = BM / 32;   // 16-row MFMA blocks per wave (wave rows: BM/2)
+  constexpr int NB = BN / 32;   // 16-column MFMA blocks per wave (wave columns: BN/2)
+  constexpr int NC = Dec::NC;   // codes a thread decodes per step
+  constexpr int RPW = 64 / NC;  // spans per weight row (threads per row)
+  constexpr int XU = BM / 32;   // 16-byte x units per loading thread per step
+  static_assert(NC == BN / 4, "one span of BN/4 codes per producer thread");
+  static_assert(RPW * BN == 256, "one span per producer thread");
+  static_assert(D >= 2, "use qmm_kernel for one iteration of prefetch");
+  extern __shared__ __attribute__((aligned(16))) uint32_t qsmem[];
+  half_t* xs = reinterpret_cast<half_t*>(qsmem);                        // [2][SUB][BM*64]
+  half_t* ws = xs + 2 * SUB * BM * kQmmBK;                              // [2][SUB][BN*64]
+  uint32_t* lut = reinterpret_cast<uint32_t*>(ws + 2 * SUB * BN * kQmmBK);  // [Dec::kLutWords]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the roles branch on scalars
+  const int pw = wave & 3;
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int t = (int)blockIdx.x;
+  const int m0 = (t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
+  const int IT = p.K / (kQmmBK * SUB);
+
+  // s_waitcnt lgkmcnt(0), the other counters free: this wave's LDS stores
+  // are done (barriers here wait for nothing else)
+  constexpr int kLdsDone = 0xC07F;
+  Dec::init_lut(lut, tid);
+
+  if (wave >= 4) {
+    // ---------------- loading and decoding waves ----------------
+    const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+    const int pt = tid & 255;
+    const int r = pt % BN, h = pt / BN;
+    const Dec dec(p, n0 + r, h);
+    struct Set {
+      u32x4 x[SUB][XU];
+      typename Dec::Raw raw[SUB];
+    };
+    Set set[D];
+    // x unit c*64 + lane of a step buffer (c = i*4 + pw) holds row
+    // (c*64+lane)/8 of the tile, 16-byte column q XOR row%8
+    auto issue = [&](int it, Set& st) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const int k0 = (it * SUB + u) * kQmmBK;
+#pragma unroll
+        for (int i = 0; i < XU; ++i) {
+          const int un = (i * 4 + pw) * 64 + lane;
+          const int row = un >> 3, q = (un & 7) ^ (row & 7);
+          const uint32_t off = 2u * ((uint32_t)(m0 + row) * (uint32_t)p.K + (uint32_t)(k0 + q * 8));
+          st.x[u][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+        }
+        dec.issue(it * SUB + u, st.raw[u]);
+      }
+    };
+    auto put = [&](int it, int buf, const Set& st) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        half_t* xb = xs + (buf * SUB + u) * BM * kQmmBK;
+#pragma unroll
+        for (int i = 0; i < XU; ++i)
+          *reinterpret_cast<u32x4*>(xb + ((i * 4 + pw) * 64 + lane) * 8) = st.x[u][i];
+        // every loaded dword stays allocated until here: a register the
+        // decode does not read would otherwise be reused while its load is
+        // in flight, and the reuse would wait for that load
+        keep_loaded(st.raw[u].d);
+        uint32_t out[NC / 2];
+        dec.decode(it * SUB + u, st.raw[u], lut, out);
+        half_t* wb = ws + (buf * SUB + u) * BN * kQmmBK;
+#pragma unroll
+        for (int q = 0; q < NC / 8; ++q)
+          *reinterpret_cast<u32x4*>(wb + qmm_swz(r, (NC / 8) * h + q) * 8) =
+              u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+      }
+    };
+    // requested in the order of the loop below (the waits the compiler
+    // places there assume the same count of loads after each set)
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      issue(min(j, IT - 1), set[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    __builtin_amdgcn_s_barrier();  // table built
+    asm volatile("" ::: "memory");
+    put(0, 0, set[0]);
+    __builtin_amdgcn_s_waitcnt(kLdsDone);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // whole rounds of D iterations (the multiplying waves skip those past
+    // IT): no exit inside the unrolled body, so that the waits the compiler
+    // places for each register set see one path through the loop
+    for (int it0 = 0; it0 < IT; it0 += D) {
+      // iteration it0 + k refills set k (its data went to LDS one iteration
+      // ago) and stores set (k+1) % D, iteration it+1
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const int it = it0 + k;
+        // the last iterations reload the last one's data and store it again
+        // (unused), so that every iteration has the same loads and waits
+        issue(min(it + D, IT - 1), set[k]);
+        put(min(it + 1, IT - 1), (it + 1) & 1, set[(k + 1) % D]);
+        __builtin_amdgcn_s_waitcnt(kLdsDone);
+        // every wave is past iteration it: buffers it&1 are free, the x and
+        // weights of it+1 are in place
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
+    return;
+  }
+
+  // ---------------- multiplying waves ----------------
+  float4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // MFMA operands of a group are all read before its first MFMA, and the
+  // group ends with a VALU read of every accumulator (see qmm_kernel)
+  constexpr int KS = kQmmBK / 32;
+  constexpr int KG = (MB + NB) <= 6 ? KS : 1;
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const half_t* xb = xs + (buf * SUB + u) * BM * kQmmBK;
+      const half_t* wb = ws + (buf * SUB + u) * BN * kQmmBK;
+#pragma unroll
+      for (int g = 0; g < KS; g += KG) {
+        half8_t af[KG][MB], bf[KG][NB];
+#pragma unroll
+        for (int kk = 0; kk < KG; ++kk) {
+          const int q = (g + kk) * 4 + (lane >> 4);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            bf[kk][j] = *reinterpret_cast<const half8_t*>(wb + qmm_swz(wn * (BN / 2) + 16 * j + (lane & 15), q) * 8);
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            af[kk][i] = *reinterpret_cast<const half8_t*>(xb + qmm_swz(wm * (BM / 2) + 16 * i + (lane & 15), q) * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t done = 0;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            done |= __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, acc[i][j][0]));
+        asm volatile("" ::"s"(done) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(kLdsDone);
+  __builtin_amdgcn_s_barrier();  // table built
+  __builtin_amdgcn_s_barrier();  // iteration 0 in place
+  asm volatile("" ::: "memory");
+  const int rounds = (IT + D - 1) / D * D;
+  for (int it = 0; it < rounds; ++it) {
+    if (it < IT) multiply(it & 1);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll

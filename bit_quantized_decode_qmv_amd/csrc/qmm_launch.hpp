@@ -28,6 +28,33 @@ int launch_qmm_s(const QmmParams& p, void* stream) {
   return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
 }
 
+// The small-M product (32-row tiles) with x and raw weight bytes requested
+// kQmmDepth iterations ahead (measured on MI355X: 4 beats 6 and 8, whose
+// register sets cost more than the extra depth brings).
+constexpr int kQmmDepth = 4;
+
+template <int BN, int BITS, int GS, bool IMPLIED, int SUB>
+int launch_qmm_deep_s(const QmmParams& p, void* stream) {
+  typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
+  const void* fn = reinterpret_cast<const void*>(&qmm_deep_kernel<32, BN, Dec, SUB, kQmmDepth>);
+  const size_t lds = qmm_deep_lds_bytes(32, BN, Dec::kLutWords, SUB);
+  static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)attr;
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + 31) / 32));
+  QmmParams q = p;
+  return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
+}
+
+// sub: K steps per iteration (4, 2 or 1), reduced to what divides the step
+// count (and to 2 for 128-column tiles: the LDS of their double buffers)
+template <int BN, int BITS, int GS, bool IMPLIED>
+int launch_qmm_deep_t(const QmmParams& p, int sub, void* stream) {
+  const int steps = p.K / kQmmBK;
+  if (BN == 64 && sub >= 4 && steps % 4 == 0) return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, (BN == 64 ? 4 : 2)>(p, stream);
+  if (sub >= 2 && steps % 2 == 0) return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, 2>(p, stream);
+  return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, 1>(p, stream);
+}
+
 // K steps per pipeline iteration of a tile shape: the small tiles (whose
 // 64-code step is much shorter than a memory round trip) take 4 (32 x 64,
 // 64 x 64) or 2 (32 x 128), as far as the LDS of one workgroup per CU and
@@ -46,10 +73,12 @@ int launch_qmm_t(const QmmParams& p, int sub, void* stream) {
 }
 
 // Small products (M <= 32, only 32-row tiles) are bound by the time of one
-// pipeline iteration, not by the MFMA or memory throughput: measured on
-// MI355X at M = 32, an iteration of SUB steps takes about 0.57 us plus
-// 0.43 us per step with 64-column tiles and 0.50 us per step with 128-column
-// tiles.  Estimated microseconds of (BN, SUB) over `tiles` workgroups (two
+// pipeline iteration, not by the MFMA or memory throughput.  Measured on
+// MI355X at M = 32 with one iteration of prefetch, an iteration of SUB steps
+// took about 0.57 us plus 0.43 us per step with 64-column tiles and 0.50 us
+// per step with 128-column tiles; the deeper prefetch now used cuts both
+// by about a third and keeps their order, which is all the choice below
+// uses.  Estimated microseconds of (BN, SUB) over `tiles` workgroups (two
 // per CU only for 32 x 64 tiles without SUB, whose LDS allows it).
 double qmm_small_m_us(int tiles, int steps, int BN, int sub) {
   const int per_cu = (BN == 64 && sub == 1) ? 2 : 1;
@@ -116,8 +145,8 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
     const Opt* o = &opts[0];
     for (const Opt& c : opts)
       if (c.us < o->us) o = &c;
-    return o->bn == 64 ? launch_qmm_t<32, 64, BITS, GS, IMPLIED>(p, o->sub, stream)
-                       : launch_qmm_t<32, 128, BITS, GS, IMPLIED>(p, o->sub, stream);
+    return o->bn == 64 ? launch_qmm_deep_t<64, BITS, GS, IMPLIED>(p, o->sub, stream)
+                       : launch_qmm_deep_t<128, BITS, GS, IMPLIED>(p, o->sub, stream);
   }
   // Rules from a measured sweep of every tile (MI355X, gate and down shapes,
   // M 17 .. 2048), where the estimate below falls short:
