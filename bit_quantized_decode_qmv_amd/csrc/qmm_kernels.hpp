@@ -2,8 +2,8 @@
 // unpacked tile by tile, from t5 bytes or from 1/2-bit uint32 codes.
 //
 // Method: "oMLX Bonsai 自定义内核" article, section 二 path 3 -- for prefill
-// with more than 16 rows the t5 weights go through a fused "unpack + matrix
-// multiply" kernel that reads each t5 byte once per weight tile.  The same
+// with more than 16 rows the t5 weights are unpacked and multiplied in one
+// fused kernel that reads each t5 byte once per weight tile.  The same
 // pipeline with a decoder for uint32 codes replaces section 二 path 1's
 // 1-bit prefill (dequantize to float16, then a matrix multiply).
 //
