@@ -287,7 +287,10 @@ def test_t5_qmm_tile_shapes_explicit_bias():
                                               # several K steps per pipeline iteration: 32 x 64 tiles
                                               # (4 steps), 64 x 64 tiles in one round (4 steps)
                                               (32, 1024, 1024, 128, "t5"), (24, 2048, 512, 64, "asym"),
-                                              (64, 4096, 768, 64, "t5"), (48, 2048, 1024, 128, "asym")])
+                                              (64, 4096, 768, 64, "t5"), (48, 2048, 1024, 128, "asym"),
+                                              # iteration counts that are not whole rounds of the
+                                              # small-M prefetch (10 and 7 steps)
+                                              (32, 2048, 640, 64, "t5"), (16, 1024, 448, 64, "asym")])
 def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
     import bit_quantized_decode_qmv_amd as bq
     inp = make("t5", M, N, K, gs, variant, seed=31)
@@ -305,6 +308,21 @@ def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
         assert len(bad) == 0, (f"K columns {base}..{base + len(ks) - 1}: {len(bad)} weights differ, e.g. "
                                + ", ".join(f"W[{n}][{ks[m]}] {y[m, n]!r} != {want[m, n]!r}" for m, n in bad[:6]))
         assert not y[len(ks):].any()
+
+
+# Products with at most 32 rows request x and weight bytes four iterations
+# ahead and walk K in whole rounds of four iterations.  K step counts of 10,
+# 7 and 21 (K 640, 448, 1344) give iteration counts that are not whole
+# rounds (one or two steps per iteration), including fewer than four.
+@pytest.mark.parametrize("M,N,K,gs", [(32, 1000, 640, 64), (32, 1000, 640, 128), (20, 515, 448, 64),
+                                      (9, 4100, 1344, 64), (32, 300, 128, 128)])
+@pytest.mark.parametrize("variant", ["t5", "asym"])
+def test_t5_qmm_small_m_partial_rounds(M, N, K, gs, variant):
+    inp = make("t5", M, N, K, gs, variant, seed=33)
+    print(f"qmm small-M rounds gs{gs} M{M} N{N} K{K} {variant}", flush=True)
+    y = run_entry("t5_qmm", inp)
+    assert np.all(np.isfinite(y))
+    assert_close(y, inp, what=f"t5_qmm small M gs{gs} M{M} K{K} {variant}")
 
 
 @pytest.mark.parametrize("shape", ["gate", "down"])

@@ -41,6 +41,18 @@ def test_qmm_parity(fmt, variant, gs, M, N, K):
     assert_close(y, inp, rows=rows, what=f"qmm {fmt} {variant} gs{gs} M{M}")
 
 
+# small-M products (at most 32 rows) walk K in whole rounds of four
+# iterations: step counts of 10, 7 and 21 leave partial rounds
+@pytest.mark.parametrize("fmt,gs,variant,M,N,K", [("u2", 64, "asym", 32, 1000, 640), ("u1", 128, "sym", 32, 1000, 640),
+                                                  ("u2", 64, "sym", 20, 515, 448), ("u1", 64, "asym", 9, 4100, 1344)])
+def test_qmm_small_m_partial_rounds(fmt, gs, variant, M, N, K):
+    inp = make(fmt, M, N, K, gs, variant, seed=93)
+    print(f"qmm small-M rounds {fmt} {variant} gs{gs} M{M} N{N} K{K}", flush=True)
+    y = run_entry("qmm", inp)
+    assert np.all(np.isfinite(y))
+    assert_close(y, inp, what=f"qmm small M {fmt} {variant} gs{gs} M{M} K{K}")
+
+
 # one-hot activation rows read every weight back exactly (one product each)
 @pytest.mark.parametrize("fmt,gs,variant,M,N,K", [("u2", 64, "asym", 20, 65536, 256), ("u1", 128, "sym", 20, 65536, 256),
                                                   ("u2", 128, "sym", 100, 65536, 256), ("u1", 64, "asym", 32, 65536, 512),
