@@ -92,6 +92,29 @@ __device__ __forceinline__ void store_pairs(half_t* dst, const uint32_t (&v)[ND]
   }
 }
 
+// The 256 threads' outputs form one contiguous block (items are in the
+// order of the output).  With 16-byte aligned output each thread puts its
+// ND dwords in LDS and the block goes out as consecutive 16-byte pieces,
+// lane after lane, so every store instruction writes 1 KB of contiguous
+// output instead of 64 pieces a thread's width apart.  `live` threads: the
+// first `nlive` of the block.
+template <int ND>
+__device__ __forceinline__ void store_block(half_t* base, const uint32_t (&v)[ND], int nlive) {
+  static_assert(ND % 4 == 0, "whole 16-byte pieces");
+  constexpr int PT = ND / 4;  // pieces per thread
+  __shared__ u32x4 stage[256 * PT];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) stage[tid * PT + i] = u32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  __syncthreads();
+  const int npieces = nlive * PT;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int piece = i * 256 + tid;
+    if (piece < npieces) reinterpret_cast<u32x4*>(base)[piece] = stage[piece];
+  }
+}
+
 // One thread per uint32 word (32/BITS codes, all inside one group).  The
 // group's 2^BITS weights are rounded once each; every code then selects
 // its weight (one v_perm_b32 per pair of codes).  A: alignment of out.
@@ -99,9 +122,12 @@ template <int BITS, bool IMPLIED, int A>
 __global__ __launch_bounds__(256) void dequant_words_kernel(DequantParams p) {
   constexpr int CPW = 32 / BITS;
   const int wpr = p.K / CPW;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)p.N * wpr) return;
-  const int row = (int)(idx / wpr);
+  const size_t total = (size_t)p.N * wpr;
+  const size_t item0 = (size_t)blockIdx.x * blockDim.x;
+  const size_t idx = item0 + threadIdx.x;
+  const bool live = idx < total;
+  if (!live && A < 16) return;  // (the 16-byte path needs every thread at its barrier)
+  const int row = live ? (int)(idx / wpr) : 0;
   const int j = (int)(idx % wpr);
   const int k0 = j * CPW;
   const int g = k0 / p.gs;
@@ -115,7 +141,11 @@ __global__ __launch_bounds__(256) void dequant_words_kernel(DequantParams p) {
 #pragma unroll
   for (int i = 0; i < CPW / 2; ++i)
     packed[i] = pair_weights(lo, hi, (word >> (BITS * (2 * i))) & mask, (word >> (BITS * (2 * i + 1))) & mask);
-  store_pairs<A>(p.out + (size_t)row * p.K + k0, packed);
+  if constexpr (A >= 16) {
+    store_block<CPW / 2>(p.out + item0 * CPW, packed, (int)min(total - item0, (size_t)256));
+  } else {
+    store_pairs<A>(p.out + (size_t)row * p.K + k0, packed);
+  }
 }
 
 // One thread per t5 group: its 13 (gs 64) or 26 (gs 128) bytes come in
@@ -126,10 +156,13 @@ template <int GS, bool IMPLIED, int A>
 __global__ __launch_bounds__(256) void dequant_t5_kernel(DequantParams p) {
   constexpr int GB = (GS + 4) / 5;        // bytes per group
   constexpr int NW = GS == 64 ? 4 : 8;    // dwords loaded
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)p.N * p.G) return;
-  const int row = (int)(idx / p.G);
-  const int g = (int)(idx % p.G);
+  const size_t total = (size_t)p.N * p.G;
+  const size_t item0 = (size_t)blockIdx.x * blockDim.x;
+  const size_t idx = item0 + threadIdx.x;
+  const bool live = idx < total;
+  if (!live && A < 16) return;  // (the 16-byte path needs every thread at its barrier)
+  const int row = live ? (int)(idx / p.G) : 0;
+  const int g = live ? (int)(idx % p.G) : 0;
   const uint32_t a = (uint32_t)row * (uint32_t)p.row_bytes + (uint32_t)(g * GB);
   // whole dwords: the dword holding W's last byte is read in full, later
   // dwords read as zeros
@@ -173,7 +206,11 @@ __global__ __launch_bounds__(256) void dequant_t5_kernel(DequantParams p) {
   uint32_t packed[GS / 2];
 #pragma unroll
   for (int t = 0; t < GS / 2; ++t) packed[t] = pair_weights(lo, hi, q[2 * t], q[2 * t + 1]);
-  store_pairs<A>(p.out + (size_t)row * p.K + (size_t)g * GS, packed);
+  if constexpr (A >= 16) {
+    store_block<GS / 2>(p.out + item0 * GS, packed, (int)min(total - item0, (size_t)256));
+  } else {
+    store_pairs<A>(p.out + (size_t)row * p.K + (size_t)g * GS, packed);
+  }
 }
 
 }  // namespace bq
