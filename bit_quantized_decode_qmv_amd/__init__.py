@@ -23,11 +23,14 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
 T5_QMM_MIN_M = 17
+T5_QMM_MIN_TILES = 64
+T5_QMM_FEW_MIN_M = 24
+T5_QMM_FEW_TILES = 16
 QMM_MIN_M = 17
 QMM_MIN_TILES = 128
 DTYPE_F16 = 1
@@ -399,7 +402,8 @@ def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
     1/2: the fused qmm from QMM_MIN_M rows when the product has
     QMM_MIN_TILES tiles, else passes of up to 5 rows through the wide or
     symmetric kernel; t5: wide passes below T5_QMM_MIN_M rows, the fused
-    qmm from there).  sym
+    qmm from there when the product has T5_QMM_MIN_TILES tiles, or
+    T5_QMM_FEW_TILES from T5_QMM_FEW_MIN_M rows).  sym
     defaults to the layer's checked symmetric-bias property."""
     use_sym = qw.sym if sym is None else sym
     M, K = x.shape
@@ -426,7 +430,7 @@ def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
 
 __all__ = [
     "ABI_VERSION", "ALL_SYMBOLS", "BITS_T5", "BQError", "DISPATCH_POINTS", "ENTRY_POINTS", "LIB_PATH",
-    "LINEAR_SYM", "MAX_WIDE_M", "QMM_MIN_M", "QMM_MIN_TILES", "QuantizedWeight", "ROUTES", "T5_QMM_MIN_M", "bq_abi_version", "bq_dequant",
+    "LINEAR_SYM", "MAX_WIDE_M", "QMM_MIN_M", "QMM_MIN_TILES", "QuantizedWeight", "ROUTES", "T5_QMM_FEW_MIN_M", "T5_QMM_FEW_TILES", "T5_QMM_MIN_M", "T5_QMM_MIN_TILES", "bq_abi_version", "bq_dequant",
     "bq_linear", "bq_linear_route", "bq_qmm", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
     "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmm", "qmv", "qmv_sym", "qmv_wide",
     "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc",

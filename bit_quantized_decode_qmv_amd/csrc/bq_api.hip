@@ -333,11 +333,16 @@ int bq_linear_route(int M, int N, int bits, int flags, int* passes) {
   if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
   int route, n = 1;
   // the fused product needs enough output tiles to occupy the GPU: with
-  // fewer, passes of up to five rows are faster (measured on the down
-  // shape, N = 5120, t5 at M = 17: about 88 us in four passes against
-  // 145 us fused)
-  const bool tiles = (int64_t)((N + 63) / 64) * ((M + 31) / 32) >= BQ_QMM_MIN_TILES;
-  if (bits == BQ_BITS_T5 && M >= BQ_T5_QMM_MIN_M && tiles) {
+  // fewer, passes of up to five rows are faster.  Measured on MI355X (gs
+  // 128, graph launches): 2-bit down (80 tiles) at M = 17 takes 87 us in
+  // four passes against 147 us fused; t5 fused at M = 17 takes 31 / 37 /
+  // 95 us on q / o / down (96 / 80 / 80 tiles) against 44 / 45 / 102 us in
+  // passes, and on k (16 tiles) 31 us against 28 us at M = 17 but 37 us
+  // in passes at M = 24.
+  const int64_t ntiles = (int64_t)((N + 63) / 64) * ((M + 31) / 32);
+  const bool tiles = ntiles >= BQ_QMM_MIN_TILES;
+  const bool t5_tiles = ntiles >= BQ_T5_QMM_MIN_TILES || (M >= BQ_T5_QMM_FEW_MIN_M && ntiles >= BQ_T5_QMM_FEW_TILES);
+  if (bits == BQ_BITS_T5 && M >= BQ_T5_QMM_MIN_M && t5_tiles) {
     route = BQ_ROUTE_T5_QMM;
   } else if (bits != BQ_BITS_T5 && M >= BQ_QMM_MIN_M && tiles) {
     route = BQ_ROUTE_QMM;

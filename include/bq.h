@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 7
+#define BQ_ABI_VERSION 8
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -86,12 +86,18 @@ typedef enum bq_status {
 /* bq_linear flags */
 #define BQ_LINEAR_SYM 1   /* bias implied (-scale*ratio; t5: -scale), biases never read */
 /* t5 calls of bq_linear with M >= BQ_T5_QMM_MIN_M take the fused qmm path
- * when the product has at least BQ_QMM_MIN_TILES tiles (below) */
+ * when the product has at least BQ_T5_QMM_MIN_TILES tiles of 32 x 64
+ * outputs, or from BQ_T5_QMM_FEW_MIN_M rows at least BQ_T5_QMM_FEW_TILES
+ * tiles (the small-M t5 product keeps four iterations of loads in flight,
+ * which makes it faster than passes of five rows on fewer tiles than the
+ * 1/2-bit product) */
 #define BQ_T5_QMM_MIN_M 17
+#define BQ_T5_QMM_MIN_TILES 64
+#define BQ_T5_QMM_FEW_MIN_M 24
+#define BQ_T5_QMM_FEW_TILES 16
 /* 1/2-bit calls of bq_linear take bq_qmm when M >= BQ_QMM_MIN_M and the
  * product has at least BQ_QMM_MIN_TILES tiles of 32 x 64 outputs
- * (ceil(N/64)*ceil(M/32)), enough to occupy half the CUs; the same tile
- * count gates the t5 fused path */
+ * (ceil(N/64)*ceil(M/32)), enough to occupy half the CUs */
 #define BQ_QMM_MIN_M 17
 #define BQ_QMM_MIN_TILES 128
 
@@ -175,8 +181,9 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
  *             bq_qmv_wide, or bq_qmv_sym when flags has BQ_LINEAR_SYM (each
  *             pass reads W once; M > 5 reads it ceil(M/5) times);
  *   t5:       bq_t5_qmm when M >= BQ_T5_QMM_MIN_M (the article's prefill
- *             rule, M > 16) and the product has BQ_QMM_MIN_TILES tiles,
- *             else passes of up to 5 rows through bq_t5_qmv_wide.
+ *             rule, M > 16) and the product has BQ_T5_QMM_MIN_TILES tiles
+ *             (or, from BQ_T5_QMM_FEW_MIN_M rows, BQ_T5_QMM_FEW_TILES
+ *             tiles), else passes of up to 5 rows through bq_t5_qmv_wide.
  * Arguments as for the entry point a pass goes to; with BQ_LINEAR_SYM the
  * biases argument is ignored (may be NULL) and the bias is implied.
  * Results are those of the entry points the passes take; each pass is

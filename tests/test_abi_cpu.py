@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 7
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 8
 
 
 def test_strerror_covers_every_status(lib):
@@ -227,15 +227,23 @@ def test_linear_routes():
         assert bq.bq_linear_route(17, 64 * 127, bits) == ("qmv_wide", 4)
         assert bq.bq_linear_route(2048, down, bits) == ("qmm", 1)
     # t5: wide passes below 17 rows, the fused product from 17 (M > 16)
-    # when there are 128 tiles of 32 x 64, as for bits 1/2
+    # when there are enough tiles of 32 x 64
     assert bq.T5_QMM_MIN_M == 17
     for M in (1, 5):
         assert bq.bq_linear_route(M, gate, bq.BITS_T5) == ("t5_qmv_wide", 1)
         assert bq.bq_linear_route(M, gate, bq.BITS_T5, bq.LINEAR_SYM) == ("t5_qmv_wide", 1)
     assert bq.bq_linear_route(16, gate, bq.BITS_T5) == ("t5_qmv_wide", 4)
+    # t5 takes the fused product on fewer tiles: 64 tiles, or 16 from 24 rows
+    assert (bq.T5_QMM_MIN_TILES, bq.T5_QMM_FEW_MIN_M, bq.T5_QMM_FEW_TILES) == (64, 24, 16)
     assert bq.bq_linear_route(17, gate, bq.BITS_T5) == ("t5_qmm", 1)
     assert bq.bq_linear_route(17, 64, bq.BITS_T5) == ("t5_qmv_wide", 4)    # 1 tile
-    assert bq.bq_linear_route(17, down, bq.BITS_T5) == ("t5_qmv_wide", 4)  # 80 tiles
+    assert bq.bq_linear_route(17, down, bq.BITS_T5) == ("t5_qmm", 1)       # 80 tiles
+    assert bq.bq_linear_route(17, 64 * 64, bq.BITS_T5) == ("t5_qmm", 1)    # 64 tiles
+    assert bq.bq_linear_route(17, 64 * 63, bq.BITS_T5) == ("t5_qmv_wide", 4)
+    assert bq.bq_linear_route(17, 1024, bq.BITS_T5) == ("t5_qmv_wide", 4)  # 16 tiles
+    assert bq.bq_linear_route(23, 1024, bq.BITS_T5) == ("t5_qmv_wide", 5)
+    assert bq.bq_linear_route(24, 1024, bq.BITS_T5) == ("t5_qmm", 1)
+    assert bq.bq_linear_route(24, 64 * 15, bq.BITS_T5) == ("t5_qmv_wide", 5)  # 15 tiles
     assert bq.bq_linear_route(33, down, bq.BITS_T5) == ("t5_qmm", 1)       # 160 tiles
     assert bq.bq_linear_route(512, gate, bq.BITS_T5) == ("t5_qmm", 1)
 

@@ -169,11 +169,13 @@ def test_linear_1_2_bit_prefill_routes(fmt, gs, M, NN):
 
 
 @pytest.mark.parametrize("gs", [64, 128])
-@pytest.mark.parametrize("M,NN", [(17, 8192), (16, 8192), (17, 5120), (40, 5120)])
+@pytest.mark.parametrize("M,NN", [(17, 8192), (16, 8192), (17, 5120), (40, 5120), (17, 4032), (23, 1024),
+                                  (24, 1024)])
 def test_linear_t5_prefill_routes(gs, M, NN):
-    """t5 from 17 rows takes the fused product when it has 128 tiles of
-    32 x 64 (17 x 8192, 40 x 5120) and gives its bits; otherwise (16 rows,
-    or 17 x 5120 with 80 tiles) five-row wide passes."""
+    """t5 from 17 rows takes the fused product when it has 64 tiles of
+    32 x 64 (17 x 8192, 17 x 5120, 40 x 5120), or 16 tiles from 24 rows
+    (24 x 1024), and gives its bits; otherwise (16 rows, 17 x 4032 with 63
+    tiles, 23 x 1024) five-row wide passes."""
     bq, torch = _bq()
     inp = make("t5", M, NN, 1024, gs, seed=102)
     qw = _qw(bq, inp, biases=None)
@@ -182,7 +184,8 @@ def test_linear_t5_prefill_routes(gs, M, NN):
     torch.cuda.synchronize()
     assert_close(y.astype(np.float64), inp, rows=np.arange(0, NN, 97), what=f"linear t5 M{M} N{NN}")
     route, passes = bq.bq_linear_route(M, NN, bq.BITS_T5)
-    expect = "t5_qmm" if (NN + 63) // 64 * ((M + 31) // 32) >= 128 and M >= 17 else "t5_qmv_wide"
+    tiles = (NN + 63) // 64 * ((M + 31) // 32)
+    expect = "t5_qmm" if M >= 17 and (tiles >= 64 or (M >= 24 and tiles >= 16)) else "t5_qmv_wide"
     assert route == expect
     if route == "t5_qmm":
         ref = to_np(bq.t5_qmm(x, qw.w, qw.scales, gs))
