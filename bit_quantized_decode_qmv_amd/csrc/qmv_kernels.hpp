@@ -39,7 +39,9 @@
 //   result scales with x.  2^-c multiplies the chunk's product sum.
 // * t5 bytes go through a 256-entry LDS table that holds a byte's five
 //   base-3 digits as 2-bit fields; two bytes fill one dword and five masks
-//   give five half2 code pairs.  13-byte runs are loaded as one dword-aligned
+//   give five half2 code pairs.  The run's single last byte is paired with
+//   itself (digits 0/1 and 2/3 in the two halves), so it costs two or three
+//   products instead of five.  13-byte runs are loaded as one dword-aligned
 //   16-byte window and realigned with v_alignbyte_b32.
 // * Epilogue per chunk: b*X + s*(P*2^-c) in fp32 (units of 2^-24), with X
 //   the chunk's (or, for 128-groups, the group's) sum of x.
@@ -120,16 +122,16 @@ template <int GS> struct Fmt<FMT_U1, GS> {
 };
 
 // t5: a chunk is 13 bytes; bytes (2p, 2p+1), p < 6, form pair p whose digit
-// i < 4 is staged at dword 4p+i and digit 4 at 28+p; byte 12 is single: its
-// digits 0..3 at dwords 24..27 and digit 4 at dword 34.
+// i < 4 is staged at dword 4p+i and digit 4 at 28+p; byte 12 is single and
+// pairs its own digits: (0, 1) at dword 24, (2, 3) at 25, digit 4 at 26.
 __device__ inline void t5_slot(int t, int i, int& d, int& h) {
   if (t < 12) {
     const int p = t >> 1;
     h = t & 1;
     d = (i < 4) ? 4 * p + i : 28 + p;
   } else {
-    h = 0;
-    d = (i < 4) ? 24 + i : 34;
+    h = i < 4 ? (i & 1) : 0;
+    d = 24 + (i >> 1);
   }
 }
 
@@ -238,6 +240,15 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t v, int k) {
   const half2_t f = __builtin_bit_cast(half2_t, v);
   const half_t sc = __builtin_bit_cast(half_t, (uint16_t)((k + 15) << 10));
   const half2_t r = f * half2_t{sc, sc};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// (lo, hi) fp16 pair times (2^klo, 2^khi), each -14 <= k <= 15.
+__device__ __forceinline__ uint32_t scale_pair2(uint32_t v, int klo, int khi) {
+  const half2_t f = __builtin_bit_cast(half2_t, v);
+  const half_t slo = __builtin_bit_cast(half_t, (uint16_t)((klo + 15) << 10));
+  const half_t shi = __builtin_bit_cast(half_t, (uint16_t)((khi + 15) << 10));
+  const half2_t r = f * half2_t{slo, shi};
   return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -371,6 +382,12 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
     const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
     return scale_pair(lo | (hi << 16), ce - e);
   };
+  // (x[k0] * 2^(ce-e0), x[k1] * 2^(ce-e1)); k < 0 means 0
+  auto P2x = [&](int k0_, int k1_, int e0, int e1) -> uint32_t {
+    const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
+    const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
+    return scale_pair2(lo | (hi << 16), ce - e0, ce - e1);
+  };
   uint32_t out[36];
 #pragma unroll
   for (int d = 0; d < 36; ++d) out[d] = 0u;
@@ -397,15 +414,16 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
 #pragma unroll
     for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
   } else if constexpr (GS == 64) {
-    // codes 0..63: pairs p < 6 hold codes 10p+i / 10p+5+i; byte 12 codes 60..63
+    // codes 0..63: pairs p < 6 hold codes 10p+i / 10p+5+i; byte 12 (codes
+    // 60..63, its digit 4 a pad) pairs its own digits: (0, 1), (2, 3)
 #pragma unroll
     for (int pr = 0; pr < 6; ++pr) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[4 * pr + i] = P2(10 * pr + i, 10 * pr + 5 + i, 2 * i);
       out[28 + pr] = P2(10 * pr + 4, 10 * pr + 9, 8);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[24 + i] = P2(60 + i, -1, 2 * i);
+    out[24] = P2x(60, 61, 0, 2);
+    out[25] = P2x(62, 63, 4, 6);
 #pragma unroll
     for (int j = 0; j < 32; ++j) sum = dot2(X(j), ones, sum);
   } else {
@@ -420,11 +438,12 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
         for (int i = 0; i < 4; ++i) out[4 * pr + i] = P2(off + 10 * pr + i, off + 10 * pr + 5 + i, 2 * i);
         out[28 + pr] = P2(off + 10 * pr + 4, off + 10 * pr + 9, 8);
       }
-      // single byte: even chunk byte 12 = codes 60..64 (5 digits); odd chunk
-      // byte 25 = codes 125..127 (3 digits) = local 60..62
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[24 + i] = P2((off == 1 && i == 3) ? -1 : off + 60 + i, -1, 2 * i);
-      out[34] = P2(off == 1 ? -1 : 64, -1, 8);
+      // single byte, its own digits paired: (0, 1), (2, 3), (4, -).  Even
+      // chunk byte 12 = codes 60..64 (5 digits); odd chunk byte 25 = codes
+      // 125..127 (3 digits) = local 60..62
+      out[24] = P2x(off + 60, off + 61, 0, 2);
+      out[25] = P2x(off + 62, off == 1 ? -1 : off + 63, 4, 6);
+      out[26] = P2x(off == 1 ? -1 : 64, -1, 8, 0);
       // sum of this half's codes: even 0..64 (span 0..64), odd 65..127 (span 1..63)
       if constexpr (off == 0) {
 #pragma unroll
@@ -524,7 +543,7 @@ __device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl,
 // Per-chunk multiply: Pd[r][m] = codes(row r) . xstaged(m).
 // xc points at the lane's staged chunk; row m of x is kXD dwords further.
 // --------------------------------------------------------------------------
-template <int FMT, int M, int R>
+template <int FMT, int GS, int M, int R>
 __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint32_t* xc,
                                           const uint16_t* lut, const uint32_t (&sh)[R], float (&Pd)[R][M]) {
   if constexpr (FMT == FMT_U2 || FMT == FMT_U1) {
@@ -600,7 +619,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           xq[(pr + 1) & 1][m] = *reinterpret_cast<const u32x4*>(xc + m * kXD + 4 * (pr + 1));
-          x4[(pr + 1) & 1][m] = xc[m * kXD + (pr + 1 < 6 ? 28 + pr + 1 : 34)];
+          if (pr + 1 < 6) x4[(pr + 1) & 1][m] = xc[m * kXD + 28 + pr + 1];
         }
       }
 #pragma unroll
@@ -611,18 +630,31 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
         if (paired) {
           const uint32_t b1 = (rb[r][t1 >> 2] >> (8 * (t1 & 3))) & 0xFFu;
           v |= (uint32_t)lut[b1] << 16;
-        }
-        const uint32_t q0 = v & 0x00030003u, q1 = v & 0x000C000Cu, q2 = v & 0x00300030u,
-                       q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
+          const uint32_t q0 = v & 0x00030003u, q1 = v & 0x000C000Cu, q2 = v & 0x00300030u,
+                         q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float acc = Pd[r][m];
-          acc = dot2(q0, xq[pr & 1][m][0], acc);
-          acc = dot2(q1, xq[pr & 1][m][1], acc);
-          acc = dot2(q2, xq[pr & 1][m][2], acc);
-          acc = dot2(q3, xq[pr & 1][m][3], acc);
-          acc = dot2(q4, x4[pr & 1][m], acc);
-          Pd[r][m] = acc;
+          for (int m = 0; m < M; ++m) {
+            float acc = Pd[r][m];
+            acc = dot2(q0, xq[pr & 1][m][0], acc);
+            acc = dot2(q1, xq[pr & 1][m][1], acc);
+            acc = dot2(q2, xq[pr & 1][m][2], acc);
+            acc = dot2(q3, xq[pr & 1][m][3], acc);
+            acc = dot2(q4, x4[pr & 1][m], acc);
+            Pd[r][m] = acc;
+          }
+        } else {
+          // the single byte pairs its own digits: (0, 1), (2, 3), and for
+          // 128-groups (4, -); 64-groups have no digit 4 in it
+          v |= v << 16;
+          const uint32_t q0 = v & 0x000C0003u, q1 = v & 0x00C00030u, q2 = v & 0x00000300u;
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float acc = Pd[r][m];
+            acc = dot2(q0, xq[pr & 1][m][0], acc);
+            acc = dot2(q1, xq[pr & 1][m][1], acc);
+            if constexpr (GS == 128) acc = dot2(q2, xq[pr & 1][m][2], acc);
+            Pd[r][m] = acc;
+          }
         }
       }
       pin_partials<R, M>(Pd);
@@ -757,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       sh[r] = ((uint32_t)(base + cg * R + r) * (uint32_t)p.row_bytes + 13u * (uint32_t)chunk) & 3u;
-    chunk_dot<FMT, M, R>(wc, xs + cs * CS, lut, sh, Pd);
+    chunk_dot<FMT, GS, M, R>(wc, xs + cs * CS, lut, sh, Pd);
     float X[M], F[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
