@@ -10,7 +10,7 @@
 // gfx950 design
 // -------------
 // * A 512-thread workgroup computes a BM x BN tile of y (BM 32 to 256, BN
-//   64 to 256, chosen per call from an estimate of its cost); the K loop
+//   64 or 128, chosen per call by rules from measured sweeps); the K loop
 //   steps 64 codes at a time.  Four waves multiply: each owns a
 //   (BM/2) x (BN/2) block and runs v_mfma_f32_16x16x32_f16 on it with fp32
 //   accumulators.  Four more waves load the next step's x and decode its
@@ -33,10 +33,11 @@
 // * Per step: the multiplying waves work on one buffer while the others fill
 //   the second one (x loads, weight decode, and the byte and scale loads of
 //   the step after); then one barrier.
-// * Small M (32-row tiles), where an iteration is far shorter than a memory
-//   round trip: a variant requests x and the raw bytes several iterations
-//   ahead into register sets, with the two kinds of waves in loops of their
-//   own (see qmm_deep_kernel).
+// * Where an iteration is far shorter than a memory round trip (small M;
+//   and the larger tiles, whose x loads one iteration ahead leave the
+//   matrix cores waiting): a variant requests x and the raw bytes several
+//   iterations ahead into register sets (see qmm_deep_kernel).
+// * In both, the two kinds of waves run loops of their own.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -167,6 +168,16 @@ __device__ __forceinline__ void t5_decode_h(int h, const uint32_t (&wv)[4], uint
   }
 }
 
+// Reads every dword of a loaded register set at the point of use.  A
+// decoder uses only some of the dwords it loads; without this the compiler
+// may give the unused ones of a load still in flight to other values, and
+// must then wait for that load before writing them.
+__device__ __forceinline__ void keep_loaded(const u32x4& d) { asm volatile("" ::"v"(d)); }
+template <int N>
+__device__ __forceinline__ void keep_loaded(const uint32_t (&d)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(d[i]));
+}
 
 // ---------------------------------------------------------------------------
 // Decoders.  A producer thread owns NC = BN/4 codes of one weight row per K
@@ -391,6 +402,7 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   const Dec dec(p, n0 + r, h);
   typename Dec::Raw raw[SUB];
   auto decode = [&](int step, int buf, int u) {  // raw bytes of sub-step u into buffer slot buf
+    keep_loaded(raw[u].d);
     uint32_t out[NC / 2];
     dec.decode(step, raw[u], lut, out);
     half_t* wb = ws + buf * BN * kQmmBK;
@@ -479,31 +491,44 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
   // (+ bias) of each of the SUB steps of the iteration after
   constexpr int kRawLoads = Dec::kRawLoads * SUB;
   static_assert(kRawLoads <= 15, "vmcnt field");
-  for (int it = 0; it < IT; ++it) {
-    const int cur = it & 1, nxt = cur ^ 1;
-    if (!producer) {
-      multiply(cur);
-    } else {
-      if (it + 1 < IT) {
+  // The two kinds of waves run loops of their own with the same barriers,
+  // so that the waits the compiler places for the loading waves' registers
+  // follow the loads those waves issued, not a state merged with the
+  // multiplying waves' path.
+  if (producer) {
+    // iterations 0 .. IT-2 prepare the next one; the last prepares nothing
+    // and is left out of the loop, which then has no branch inside (a
+    // branch around the preparing part would make the compiler see a path
+    // on which this pass's loads meet the next pass's with the registers
+    // still in flight, and wait for them on every pass)
+    for (int it = 0; it + 1 < IT; ++it) {
+      const int nxt = (it & 1) ^ 1;
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) issue_x((it + 1) * SUB + u, nxt * SUB + u);
+      for (int u = 0; u < SUB; ++u) issue_x((it + 1) * SUB + u, nxt * SUB + u);
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) decode((it + 1) * SUB + u, nxt * SUB + u, u);
-      }
-      // always issued (the last iterations reload the last step's bytes,
-      // unused), so that the count of loads after the x loads is fixed
+      for (int u = 0; u < SUB; ++u) decode((it + 1) * SUB + u, nxt * SUB + u, u);
+      // always issued (the last pass reloads the last step's bytes,
+      // unused), so that the count of loads after the x loads is fixed; not
+      // moved above the decode, which would need the registers they fill
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < SUB; ++u) dec.issue(min((it + 2) * SUB + u, S - 1), raw[u]);
       // this wave's x loads of iteration it+1 have landed in LDS (only the
       // loads issued after them may still be in flight), its weight stores
       // are done
       __builtin_amdgcn_s_waitcnt(0x0070 | kRawLoads);  // vmcnt(kRawLoads), lgkmcnt(0)
+      // every wave is past iteration it: buffer it&1 is free, buffer nxt is full
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-    // every wave is past iteration it: buffer cur is free, buffer nxt is full
+    __builtin_amdgcn_s_barrier();  // the multiplying waves' last iteration
+    return;
+  }
+  for (int it = 0; it < IT; ++it) {
+    multiply(it & 1);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  if (producer) return;
 
   // D layout of 16x16x32: lane holds rows 4*(lane/16)+v, column lane%16
 #pragma unroll
@@ -520,8 +545,9 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
 
 
 // ---------------------------------------------------------------------------
-// The product for small M (32-row tiles), where one K iteration of a tile is
-// far shorter than a memory round trip.  Same work split and LDS layout as
+// The product where one K iteration of a tile is shorter than a memory round
+// trip: 32-row tiles (small M), and the larger tiles too, whose iterations
+// do not cover a round trip either.  Same work split and LDS layout as
 // qmm_kernel, but the loading waves request x and the raw weight bytes D
 // iterations ahead, into D register sets, and store an iteration's x to LDS
 // (next to its decoded weights) one iteration before it is multiplied.  An
@@ -535,13 +561,6 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_kernel(QmmParams p) {
 // The products and their order are those of qmm_kernel, so the output is
 // the same bit for bit.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void keep_loaded(const u32x4& d) { asm volatile("" ::"v"(d)); }
-template <int N>
-__device__ __forceinline__ void keep_loaded(const uint32_t (&d)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(d[i]));
-}
-
 constexpr size_t qmm_deep_lds_bytes(int BM, int BN, int lut_words, int SUB) { return qmm_lds_bytes(BM, BN, lut_words, SUB); }
 
 template <int BM, int BN, class Dec, int SUB, int D>

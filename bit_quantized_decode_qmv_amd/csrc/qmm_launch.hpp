@@ -16,6 +16,7 @@ template <int BN, int BITS, int GS, bool IMPLIED>
 using QmmDecoder = typename std::conditional<BITS == BQ_BITS_T5, T5Decoder<BN, GS, IMPLIED>,
                                              UqDecoder<BN, (BITS == 1 ? 1 : 2), GS, IMPLIED>>::type;
 
+// x staged through LDS by direct loads, requested one iteration ahead
 template <int BM, int BN, int BITS, int GS, bool IMPLIED, int SUB>
 int launch_qmm_s(const QmmParams& p, void* stream) {
   typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
@@ -28,48 +29,36 @@ int launch_qmm_s(const QmmParams& p, void* stream) {
   return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
 }
 
-// The small-M product (32-row tiles) with x and raw weight bytes requested
-// kQmmDepth iterations ahead (measured on MI355X: 4 beats 6 and 8, whose
-// register sets cost more than the extra depth brings).
-constexpr int kQmmDepth = 4;
-
-template <int BN, int BITS, int GS, bool IMPLIED, int SUB>
+// x and the raw weight bytes requested D iterations ahead into registers
+template <int BM, int BN, int BITS, int GS, bool IMPLIED, int SUB, int D>
 int launch_qmm_deep_s(const QmmParams& p, void* stream) {
   typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
-  const void* fn = reinterpret_cast<const void*>(&qmm_deep_kernel<32, BN, Dec, SUB, kQmmDepth>);
-  const size_t lds = qmm_deep_lds_bytes(32, BN, Dec::kLutWords, SUB);
+  const void* fn = reinterpret_cast<const void*>(&qmm_deep_kernel<BM, BN, Dec, SUB, D>);
+  const size_t lds = qmm_deep_lds_bytes(BM, BN, Dec::kLutWords, SUB);
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
-  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + 31) / 32));
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   QmmParams q = p;
   return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
 }
+
+// Small products (M <= 32, 32-row tiles) request x and the weight bytes
+// kQmmDepth iterations ahead (measured on MI355X: 4 beats 6 and 8, whose
+// register sets cost more than the extra depth brings); larger tiles
+// kQmmDepthWide (2: measured no slower than 3 or 4 on any tile, and its
+// register sets leave the 128 x 64 tile two workgroups per CU).
+constexpr int kQmmDepth = 4;
+constexpr int kQmmDepthWide = 2;
 
 // sub: K steps per iteration (4, 2 or 1), reduced to what divides the step
 // count (and to 2 for 128-column tiles: the LDS of their double buffers)
 template <int BN, int BITS, int GS, bool IMPLIED>
 int launch_qmm_deep_t(const QmmParams& p, int sub, void* stream) {
   const int steps = p.K / kQmmBK;
-  if (BN == 64 && sub >= 4 && steps % 4 == 0) return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, (BN == 64 ? 4 : 2)>(p, stream);
-  if (sub >= 2 && steps % 2 == 0) return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, 2>(p, stream);
-  return launch_qmm_deep_s<BN, BITS, GS, IMPLIED, 1>(p, stream);
-}
-
-// K steps per pipeline iteration of a tile shape: the small tiles (whose
-// 64-code step is much shorter than a memory round trip) take 4 (32 x 64,
-// 64 x 64) or 2 (32 x 128), as far as the LDS of one workgroup per CU and
-// the step count K/64 allow; the others 1.
-constexpr int qmm_sub(int BM, int BN) { return (BM <= 64 && BN == 64) ? 4 : (BM == 32 && BN == 128) ? 2 : 1; }
-
-// sub: the K steps per iteration wanted (4, 2 or 1); reduced to what the
-// tile's LDS allows (qmm_sub) and what divides the step count
-template <int BM, int BN, int BITS, int GS, bool IMPLIED>
-int launch_qmm_t(const QmmParams& p, int sub, void* stream) {
-  constexpr int SUB = qmm_sub(BM, BN);
-  const int steps = p.K / kQmmBK;
-  if (sub >= 4 && SUB >= 4 && steps % 4 == 0) return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, (SUB >= 4 ? 4 : 1)>(p, stream);
-  if (sub >= 2 && SUB >= 2 && steps % 2 == 0) return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, (SUB >= 2 ? 2 : 1)>(p, stream);
-  return launch_qmm_s<BM, BN, BITS, GS, IMPLIED, 1>(p, stream);
+  if (BN == 64 && sub >= 4 && steps % 4 == 0)
+    return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, (BN == 64 ? 4 : 2), kQmmDepth>(p, stream);
+  if (sub >= 2 && steps % 2 == 0) return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, 2, kQmmDepth>(p, stream);
+  return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, 1, kQmmDepth>(p, stream);
 }
 
 // Small products (M <= 32, only 32-row tiles) are bound by the time of one
@@ -87,49 +76,8 @@ double qmm_small_m_us(int tiles, int steps, int BN, int sub) {
   return rounds * ((double)steps / sub) * iter;
 }
 
-// Estimated cycles of one call with BM x BN tiles: per K step the larger of
-// the MFMA cycles and the LDS cycles (operand reads, tile writes), plus the
-// weight-decoding ALU cycles (measured not to overlap the MFMAs; alu_per_col
-// per weight row of the tile), times the rounds of workgroups over 256 CUs;
-// against the L2 / last-level-cache traffic of re-reading x once per column
-// of tiles and W (w_bytes_per_weight) once per row of tiles at 32 bytes per
-// clock per CU.  Only the order of the estimates matters: it picks the tile
-// shape.
-double qmm_cost(int M, int N, int K, int BM, int BN, int lut_words, double alu_per_col,
-                double w_bytes_per_weight) {
-  const double mfma = (double)BM * BN / 32.0;
-  const double lds = 64.0 * (BM / 32 + BN / 32) + (BM + BN);
-  const double alu = alu_per_col * BN;
-  const double step = std::max(mfma, lds) + alu;
-  const double tiles = (double)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-  const int per_cu = qmm_lds_bytes(BM, BN, lut_words) * 2 <= 160 * 1024 ? 2 : 1;
-  const double rounds = std::ceil(tiles / (256.0 * per_cu));
-  const double compute = rounds * per_cu * (K / kQmmBK) * step;
-  const double traffic = ((double)M * K * 2 * ((N + BN - 1) / BN) +
-                          (double)N * K * w_bytes_per_weight * ((M + BM - 1) / BM)) /
-                         (256.0 * 32.0);
-  return std::max(compute, traffic);
-}
-
 template <int BITS, int GS, bool IMPLIED>
 int launch_qmm_m(const QmmParams& p, void* stream) {
-  typedef int (*Fn)(const QmmParams&, int, void*);
-  struct Cand {
-    int bm, bn;
-    Fn fn;
-  };
-  // the shapes the estimate picks over M 1..4096, N 256..65536, K 256..17408
-  // (128 x 256 tiles, which it picks for a few, do not fit the registers of
-  // the two wave kinds)
-  static const Cand cands[] = {
-      {32, 64, &launch_qmm_t<32, 64, BITS, GS, IMPLIED>},   {32, 128, &launch_qmm_t<32, 128, BITS, GS, IMPLIED>},
-      {64, 64, &launch_qmm_t<64, 64, BITS, GS, IMPLIED>},   {64, 256, &launch_qmm_t<64, 256, BITS, GS, IMPLIED>},
-      {128, 64, &launch_qmm_t<128, 64, BITS, GS, IMPLIED>}, {256, 64, &launch_qmm_t<256, 64, BITS, GS, IMPLIED>},
-      {256, 128, &launch_qmm_t<256, 128, BITS, GS, IMPLIED>},
-  };
-  const int lut_words = QmmDecoder<64, BITS, GS, IMPLIED>::kLutWords;
-  const double alu = BITS == BQ_BITS_T5 ? 2.5 : 1.5;
-  const double wbytes = BITS == BQ_BITS_T5 ? 0.2 : BITS / 8.0;
   const int steps = p.K / kQmmBK;
   if (p.M <= 32) {
     // 32 x 64 (SUB 1 or 4) or 32 x 128 (SUB 1 or 2), whichever the measured
@@ -148,36 +96,32 @@ int launch_qmm_m(const QmmParams& p, void* stream) {
     return o->bn == 64 ? launch_qmm_deep_t<64, BITS, GS, IMPLIED>(p, o->sub, stream)
                        : launch_qmm_deep_t<128, BITS, GS, IMPLIED>(p, o->sub, stream);
   }
-  // Rules from a measured sweep of every tile (MI355X, gate and down shapes,
-  // M 17 .. 2048), where the estimate below falls short:
-  // * when all 32 x 64 tiles run at once (one per CU), that tile with 4
-  //   steps per iteration (down: M = 48 214 -> 143 us, M = 96 213 -> 143);
-  // * else when all 64 x 64 tiles do, that tile with 4 steps per iteration
-  //   (down: M = 128 215 -> 156 us);
-  // * with 256 to 512 tiles of 128 x 64 (two per CU, all resident) and more
-  //   than 64 rows, that tile (down, M = 512: 295 -> 262 us); with fewer
-  //   tiles it is slower than the estimate's choice.
+  // Rules from a measured sweep of seven tiles and prefetch depths 1-4
+  // (MI355X; q 6144 x 5120, gate 17408 x 5120, down 5120 x 17408; t5 and
+  // 2-bit; M 64 .. 2048), in microseconds per call:
+  // * when all 32 x 64 tiles (or else all 64 x 64 tiles) run at once, one
+  //   per CU, that tile with 4 steps per iteration and x one iteration
+  //   ahead (t5 q M = 64: 32 us, down M = 128: 117 us);
+  // * else up to 64 rows: 64 x 64 tiles, two iterations ahead (gate M = 64:
+  //   t5 69 -> 63, 2-bit 63 -> 62);
+  // * t5: 128 x 64 tiles two iterations ahead (two workgroups per CU): M =
+  //   256 q 61 -> 48, M = 512 gate 226 -> 171, M = 2048 down 735 -> 608;
+  // * 1/2-bit, whose per-row decode costs more on 64-column tiles: above
+  //   512 rows 256 x 128 tiles (M = 2048 q 242 -> 219, gate 601 -> 544,
+  //   down 767 -> 709), above 256 rows of at most 8192 columns 256 x 64
+  //   (q M = 512: 92 -> 80), else 128 x 64 (q M = 256: 78 -> 55, gate M =
+  //   512: 234 -> 198); all two iterations ahead.
   const int t32 = ((p.M + 31) / 32) * ((p.N + 63) / 64);
   const int t64 = ((p.M + 63) / 64) * ((p.N + 63) / 64);
-  const int t128 = ((p.M + 127) / 128) * ((p.N + 63) / 64);
-  if (steps % 4 == 0 && t32 <= 256) return launch_qmm_t<32, 64, BITS, GS, IMPLIED>(p, 4, stream);
-  if (steps % 4 == 0 && t64 <= 256) return launch_qmm_t<64, 64, BITS, GS, IMPLIED>(p, 4, stream);
-  if (p.M > 64 && t128 > 256 && t128 <= 512) return launch_qmm_t<128, 64, BITS, GS, IMPLIED>(p, 1, stream);
-  const Cand* best = nullptr;
-  double best_cost = 0.0;
-  for (const Cand& c : cands) {
-    if (c.bm > 32 && c.bm / 2 >= p.M) continue;  // a tile at least half full of rows
-    const double cost = qmm_cost(p.M, p.N, p.K, c.bm, c.bn, lut_words, alu, wbytes);
-    if (!best || cost < best_cost) {
-      best = &c;
-      best_cost = cost;
-    }
+  if (steps % 4 == 0 && t32 <= 256) return launch_qmm_s<32, 64, BITS, GS, IMPLIED, 4>(p, stream);
+  if (steps % 4 == 0 && t64 <= 256) return launch_qmm_s<64, 64, BITS, GS, IMPLIED, 4>(p, stream);
+  constexpr int D = kQmmDepthWide;
+  if (p.M <= 64) return launch_qmm_deep_s<64, 64, BITS, GS, IMPLIED, 1, D>(p, stream);
+  if (BITS != BQ_BITS_T5) {
+    if (p.M > 512) return launch_qmm_deep_s<256, 128, BITS, GS, IMPLIED, 1, D>(p, stream);
+    if (p.M > 256 && p.N <= 8192) return launch_qmm_deep_s<256, 64, BITS, GS, IMPLIED, 1, D>(p, stream);
   }
-  // the 64 x 64 tile iterates over SUB = 4 steps when all its workgroups run
-  // at once (one per CU: its LDS then holds no second workgroup)
-  const int tiles = ((p.N + best->bn - 1) / best->bn) * ((p.M + best->bm - 1) / best->bm);
-  const int sub = (best->bm == 64 && best->bn == 64 && tiles <= 256) ? 4 : 1;
-  return best->fn(p, sub, stream);
+  return launch_qmm_deep_s<128, 64, BITS, GS, IMPLIED, 1, D>(p, stream);
 }
 
 template <int BITS>

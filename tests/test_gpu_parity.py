@@ -256,13 +256,17 @@ def test_t5_qmm_matches_wide():
     assert ok, worst
 
 
-# Shapes for which the tile choice takes each tile shape the library has
-# (32x64 is taken by the small cases above): 32x128, 64x64, 128x64, 64x256,
-# 256x64, 256x128 (also with a ragged row count); checked on sampled output
-# columns.
+# Shapes for which the tile choice takes each route above 32 rows: 32 x 64
+# and 64 x 64 tiles with four steps per iteration and x one iteration ahead
+# (40 x 4096, 80 x 8192), 64 x 64 tiles two iterations ahead (40 and 50 rows
+# of wide N; 50 x 1000 with 6 K steps, no multiple of four), 128 x 64 tiles
+# two iterations ahead (the rest; 100 x 200 with 2 K steps, as many
+# iterations as the prefetch depth); ragged row and column counts; checked
+# on sampled output columns.
 @pytest.mark.parametrize("gs", [64, 128])
-@pytest.mark.parametrize("M,N,K", [(20, 65536, 256), (40, 17408, 256), (80, 17408, 256), (50, 65536, 256),
-                                   (100, 65536, 256), (160, 12288, 256), (600, 17408, 1024)])
+@pytest.mark.parametrize("M,N,K", [(20, 65536, 256), (40, 4096, 256), (80, 8192, 256), (40, 17408, 256),
+                                   (50, 65536, 256), (50, 1000, 384), (80, 17408, 256), (100, 65536, 256),
+                                   (100, 200, 128), (160, 12288, 256), (600, 17408, 1024)])
 def test_t5_qmm_tile_shapes(gs, M, N, K):
     inp = make("t5", M, N, K, gs, "t5", seed=23)
     print(f"qmm tiles gs{gs} M{M} N{N} K{K}", flush=True)
@@ -290,7 +294,10 @@ def test_t5_qmm_tile_shapes_explicit_bias():
                                               (64, 4096, 768, 64, "t5"), (48, 2048, 1024, 128, "asym"),
                                               # iteration counts that are not whole rounds of the
                                               # small-M prefetch (10 and 7 steps)
-                                              (32, 2048, 640, 64, "t5"), (16, 1024, 448, 64, "asym")])
+                                              (32, 2048, 640, 64, "t5"), (16, 1024, 448, 64, "asym"),
+                                              # a single K step: fewer iterations than the
+                                              # prefetch depth of 128 x 64 tiles
+                                              (100, 200, 64, 64, "t5")])
 def test_t5_qmm_one_hot_rows_read_exact_weights(M, N, K, gs, variant):
     import bit_quantized_decode_qmv_amd as bq
     inp = make("t5", M, N, K, gs, variant, seed=31)

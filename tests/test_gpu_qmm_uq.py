@@ -26,12 +26,19 @@ def _sample_rows(N, seed):
     return np.array(sorted(rows))
 
 
-# shapes that reach every tile shape of the cost estimate, ragged M and N
+# shapes that reach every route of the tile choice, ragged M and N: 32-row
+# tiles (M <= 32); 32 x 64 and 64 x 64 tiles with four steps per iteration
+# (130 x 129, 80 x 8192); 64 x 64 tiles two iterations ahead (40 x 17408;
+# 50 x 1000 with 6 K steps); 128 x 64 (100 and 160 rows; 100 x 200 with 2 K
+# steps), 256 x 64 (300 x 8000) and 256 x 128 tiles (600 and 520 rows), two
+# iterations ahead
 @pytest.mark.parametrize("fmt", ["u1", "u2"])
 @pytest.mark.parametrize("variant", ["asym", "sym"])
 @pytest.mark.parametrize("gs", [64, 128])
 @pytest.mark.parametrize("M,N,K", [(1, 40, 256), (17, 200, 512), (20, 65536, 256), (40, 17408, 256),
-                                   (130, 129, 1024), (100, 65536, 256), (160, 12288, 256), (600, 17408, 1024)])
+                                   (50, 1000, 384), (80, 8192, 256), (130, 129, 1024), (100, 65536, 256),
+                                   (100, 200, 128), (160, 12288, 256), (300, 8000, 512), (520, 130, 384),
+                                   (600, 17408, 1024)])
 def test_qmm_parity(fmt, variant, gs, M, N, K):
     inp = make(fmt, M, N, K, gs, variant, seed=90)
     print(f"qmm {fmt} {variant} gs{gs} M{M} N{N} K{K}", flush=True)
@@ -57,6 +64,10 @@ def test_qmm_small_m_partial_rounds(fmt, gs, variant, M, N, K):
 @pytest.mark.parametrize("fmt,gs,variant,M,N,K", [("u2", 64, "asym", 20, 65536, 256), ("u1", 128, "sym", 20, 65536, 256),
                                                   ("u2", 128, "sym", 100, 65536, 256), ("u1", 64, "asym", 32, 65536, 512),
                                                   ("u2", 64, "sym", 300, 16384, 512),
+                                                  # 256 x 64 and 256 x 128 tiles
+                                                  ("u1", 128, "sym", 300, 4096, 512), ("u2", 64, "asym", 520, 2048, 768),
+                                                  # a single K step (fewer iterations than the prefetch depth)
+                                                  ("u2", 64, "asym", 100, 200, 64), ("u1", 64, "sym", 600, 130, 64),
                                                   # several K steps per pipeline iteration (32 x 64, 64 x 64)
                                                   ("u2", 128, "asym", 32, 1024, 1024), ("u1", 64, "sym", 24, 2048, 512),
                                                   ("u2", 64, "asym", 64, 4096, 768), ("u1", 128, "asym", 48, 2048, 1024)])
