@@ -49,6 +49,7 @@ Other modes:
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -348,7 +349,8 @@ def launch_set_specs(name):
     if name == "t5":
         return [("bq_t5_qmv_wide", "t5", "t5", M, s, gs) for gs in GROUP_SIZES for M in (1, 5) for s in SHAPES]
     if name == "qmm":
-        return [("bq_t5_qmm", "t5", "t5", M, s, 128) for s in ("gate", "down") for M in (32, 512, 2048)]
+        return ([("bq_t5_qmm", "t5", "t5", M, s, 128) for s in ("gate", "down") for M in (32, 512, 2048)]
+                + [("bq_t5_qmm_ws", "t5", "t5", 32, s, 128) for s in ("gate", "down")])
     if name == "dequant":
         return [("bq_dequant", f, "asym" if f != "t5" else "t5", 0, s, 64) for f in ("u1", "u2", "t5")
                 for s in ("gate", "down")]
@@ -377,6 +379,15 @@ def launch_set_run(torch, lib, dev, name):
             st = lib.bq_dequant(None, w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None,
                                 y.data_ptr(), 0, N, K, inp.bits, gs, h)
             nb = w.numel() * w.element_size() + s.numel() * 2 * (2 if b is not None else 1) + N * K * 2
+        elif entry == "bq_t5_qmm_ws":
+            # the K-split product: its kernel and the partial-sum kernel
+            c = Call(torch, "bq_t5_qmm", fmt, variant, M, N, K, gs, (x, w, s, b), "")
+            need = ctypes.c_size_t(0)
+            st = lib.bq_qmm_workspace(M, N, K, inp.bits, gs, ctypes.byref(need))
+            ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+            px, pw, ps, pb, py = c.ptrs
+            st = st or lib.bq_t5_qmm_ws(px, pw, ps, pb, py, M, N, K, inp.bits, gs, ws.data_ptr(), need.value, h)
+            nb = c.bytes
         else:
             c = Call(torch, entry, fmt, variant, M, N, K, gs, (x, w, s, b), "")
             st = 0

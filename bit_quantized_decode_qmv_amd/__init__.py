@@ -23,7 +23,7 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1
@@ -44,7 +44,8 @@ LIB_PATH = os.path.join(_PKG_DIR, "libbq.so")
 ENTRY_POINTS = ("bq_qmv", "bq_qmv_wide", "bq_qmv_sym", "bq_t5_qmv", "bq_t5_qmv_wide",
                 "bq_t5_qmm", "bq_dequant", "bq_qmm")
 DISPATCH_POINTS = ("bq_linear", "bq_linear_route", "bq_sym_check", "bq_t5_repack", "bq_spec_verify_workspace",
-                   "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc")
+                   "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc", "bq_qmm_workspace", "bq_t5_qmm_ws",
+                   "bq_qmm_ws", "bq_linear_ws")
 ALL_SYMBOLS = ("bq_abi_version", "bq_strerror") + ENTRY_POINTS + DISPATCH_POINTS
 
 STATUS = {
@@ -96,6 +97,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bq_spec_decode_verify.argtypes = [vp, i, vp, i, i, i, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bq_spec_decode_verify_noalloc.restype = ctypes.c_int
     lib.bq_spec_decode_verify_noalloc.argtypes = [vp, i, vp, i, i, i, vp, vp, vp, vp]
+    lib.bq_linear_ws.restype = ctypes.c_int
+    lib.bq_linear_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, ctypes.c_size_t, vp]
+    lib.bq_qmm_workspace.restype = ctypes.c_int
+    lib.bq_qmm_workspace.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    for name in ("bq_t5_qmm_ws", "bq_qmm_ws"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, ctypes.c_size_t, vp]
     ver = lib.bq_abi_version()
     if ver != ABI_VERSION:
         raise ImportError(f"{p} has ABI version {ver}, this binding needs {ABI_VERSION}")
@@ -150,6 +159,13 @@ def bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags, stream=
                                                stream), "bq_linear")
 
 
+def bq_linear_ws(x, w, scales, biases, y, M, N, K, bits, group_size, flags, workspace, workspace_bytes,
+                 stream=None):
+    """C entry point bq_linear_ws of include/bq.h (pointers and stream as integers)."""
+    return _raise_if(load_library().bq_linear_ws(x, w, scales, biases, y, M, N, K, bits, group_size, flags,
+                                                  workspace, workspace_bytes, stream), "bq_linear_ws")
+
+
 def bq_linear_route(M, N, bits, flags=0):
     """(route name, passes) bq_linear takes for (M, N, bits, flags); host only."""
     passes = ctypes.c_int(0)
@@ -191,6 +207,25 @@ def bq_spec_decode_verify_noalloc(logits, logits_dtype, draft, B, L, V, accepted
     return _raise_if(load_library().bq_spec_decode_verify_noalloc(logits, logits_dtype, draft, B, L, V, accepted,
                                                                   next_token, target_tokens, stream),
                      "bq_spec_decode_verify_noalloc")
+
+
+def bq_qmm_workspace(M, N, K, bits, group_size):
+    """Workspace bytes the K-split prefill products want (0: no split; host only)."""
+    n = ctypes.c_size_t(0)
+    _raise_if(load_library().bq_qmm_workspace(M, N, K, bits, group_size, ctypes.byref(n)), "bq_qmm_workspace")
+    return n.value
+
+
+def bq_t5_qmm_ws(x, w, scales, biases, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream=None):
+    """C entry point bq_t5_qmm_ws of include/bq.h (pointers and stream as integers)."""
+    return _raise_if(load_library().bq_t5_qmm_ws(x, w, scales, biases, y, M, N, K, bits, group_size, workspace,
+                                                  workspace_bytes, stream), "bq_t5_qmm_ws")
+
+
+def bq_qmm_ws(x, w, scales, biases, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream=None):
+    """C entry point bq_qmm_ws of include/bq.h (pointers and stream as integers)."""
+    return _raise_if(load_library().bq_qmm_ws(x, w, scales, biases, y, M, N, K, bits, group_size, workspace,
+                                               workspace_bytes, stream), "bq_qmm_ws")
 
 
 # ---------------------------------------------------------------------------
@@ -290,6 +325,44 @@ def qmm(x, w, scales, bits: int, group_size: int, biases=None, out=None):
     -scale*(2^bits-1)/2)."""
     M, N, K = _shapes(x, scales, group_size)
     return _run("bq_qmm", x, w, scales, biases, bits, group_size, out, M, N, K, (M, N))
+
+
+def _run_ws(name, x, w, scales, biases, bits, group_size, out, workspace):
+    torch = _torch()
+    M, N, K = _shapes(x, scales, group_size)
+    dev = w.device
+    _check(w, "w", torch.uint8 if bits == BITS_T5 else torch.int32, dev)
+    _check(scales, "scales", torch.float16, dev)
+    _check(x, "x", torch.float16, dev)
+    if biases is not None:
+        _check(biases, "biases", torch.float16, dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    else:
+        _check(out, "out", torch.float16, dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    if workspace is None:
+        need = bq_qmm_workspace(M, N, K, bits, group_size)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    elif workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    fn = bq_t5_qmm_ws if name == "bq_t5_qmm_ws" else bq_qmm_ws
+    fn(x.data_ptr(), w.data_ptr(), scales.data_ptr(), biases.data_ptr() if biases is not None else None,
+       out.data_ptr(), M, N, K, bits, group_size, workspace.data_ptr() if workspace is not None else None,
+       workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream_handle(dev))
+    return out
+
+
+def t5_qmm_ws(x, w, scales, group_size: int, biases=None, out=None, workspace=None):
+    """t5 prefill product with K split over a workspace (a device tensor of
+    at least bq_qmm_workspace bytes, 16-byte aligned; None: allocated here)."""
+    return _run_ws("bq_t5_qmm_ws", x, w, scales, biases, BITS_T5, group_size, out, workspace)
+
+
+def qmm_ws(x, w, scales, bits: int, group_size: int, biases=None, out=None, workspace=None):
+    """1/2-bit prefill product with K split over a workspace (as t5_qmm_ws)."""
+    return _run_ws("bq_qmm_ws", x, w, scales, biases, bits, group_size, out, workspace)
 
 
 def dequant(w, scales, biases, bits: int, group_size: int, K: int, out=None):
@@ -397,14 +470,17 @@ class QuantizedWeight:
         return QuantizedWeight(w5, self.scales, None if implied else self.biases, BITS_T5, self.group_size)
 
 
-def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
+def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None, workspace=None):
     """y = x . W^T for any number of rows, routed as bq_linear does (bits
     1/2: the fused qmm from QMM_MIN_M rows when the product has
     QMM_MIN_TILES tiles, else passes of up to 5 rows through the wide or
     symmetric kernel; t5: wide passes below T5_QMM_MIN_M rows, the fused
     qmm from there when the product has T5_QMM_MIN_TILES tiles, or
     T5_QMM_FEW_TILES from T5_QMM_FEW_MIN_M rows).  sym
-    defaults to the layer's checked symmetric-bias property."""
+    defaults to the layer's checked symmetric-bias property.  workspace:
+    None (bq_linear), a device tensor, or "auto" (allocated here, of the
+    bq_qmm_workspace size): routed as bq_linear_ws, the fused product with
+    K split from QMM_MIN_M / T5_QMM_MIN_M rows."""
     use_sym = qw.sym if sym is None else sym
     M, K = x.shape
     if K != qw.K:
@@ -422,9 +498,20 @@ def linear(x, qw: QuantizedWeight, out=None, sym: Optional[bool] = None):
         _check(out, "out", torch.float16, dev)
         if tuple(out.shape) != (M, qw.N):
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, qw.N)}")
-    bq_linear(x.data_ptr(), qw.w.data_ptr(), qw.scales.data_ptr(),
-              qw.biases.data_ptr() if qw.biases is not None else None, out.data_ptr(), M, qw.N, qw.K, qw.bits,
-              qw.group_size, LINEAR_SYM if use_sym else 0, _stream_handle(dev))
+    args = (x.data_ptr(), qw.w.data_ptr(), qw.scales.data_ptr(),
+            qw.biases.data_ptr() if qw.biases is not None else None, out.data_ptr(), M, qw.N, qw.K, qw.bits,
+            qw.group_size, LINEAR_SYM if use_sym else 0)
+    if workspace is None:
+        bq_linear(*args, _stream_handle(dev))
+        return out
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be None, 'auto' or a tensor, got {workspace!r}")
+        need = bq_qmm_workspace(M, qw.N, qw.K, qw.bits, qw.group_size)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    bq_linear_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(dev))
     return out
 
 
@@ -434,6 +521,7 @@ __all__ = [
     "bq_linear", "bq_linear_route", "bq_qmm", "bq_qmv", "bq_qmv_sym", "bq_qmv_wide", "bq_sym_check", "bq_t5_qmm",
     "bq_t5_qmv", "bq_t5_qmv_wide", "dequant", "linear", "load_library", "qmm", "qmv", "qmv_sym", "qmv_wide",
     "DTYPE_F16", "DTYPE_F32", "SPEC_MAX_DRAFT", "bq_spec_decode_verify", "bq_spec_decode_verify_noalloc",
-    "bq_spec_verify_workspace",
+    "bq_spec_verify_workspace", "bq_qmm_workspace", "bq_qmm_ws", "bq_t5_qmm_ws", "qmm_ws", "t5_qmm_ws",
+    "bq_linear_ws",
     "bq_t5_repack", "spec_decode_verify", "strerror", "sym_check", "t5_qmm", "t5_qmv", "t5_qmv_wide", "t5_repack",
 ]

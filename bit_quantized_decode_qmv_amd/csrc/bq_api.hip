@@ -172,8 +172,11 @@ int run_qmv(Entry e, const void* x, const void* w, const void* scales, const voi
 
 // ---------------------------------------------------------------- qmm
 int launch_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
-               int K, int bits, int group_size, void* stream) {
+               int K, int bits, int group_size, void* stream, void* workspace = nullptr, size_t ws_bytes = 0) {
   QmmParams p{};
+  p.ksplit = 1;
+  p.part = static_cast<float*>(workspace);
+  p.part_cap = workspace ? ws_bytes : 0;
   p.x = static_cast<const half_t*>(x);
   p.w = static_cast<const uint8_t*>(w);
   p.s = static_cast<const half_t*>(scales);
@@ -244,8 +247,9 @@ const char* bq_strerror(int status) {
       return "N and K must be positive, K a multiple of group_size, and the sizes within the limits of bq.h";
     case BQ_ERR_M: return "M is outside the range this entry point accepts";
     case BQ_ERR_ALIGN:
-      return "a pointer is misaligned (W 4 bytes; x, scales and biases of the decode calls 4 bytes; x of the "
-             "prefill products 16 bytes; fp16 outputs 2 bytes), or a t5 repack has K not a multiple of 256";
+      return "a pointer is misaligned (W 4 bytes; x, scales and biases of the decode calls 4 bytes; x and the "
+             "workspace of the prefill products 16 bytes; fp16 outputs 2 bytes), or a t5 repack has K not a "
+             "multiple of 256";
     case BQ_ERR_FLAGS: return "flags holds bits this entry point does not define";
     case BQ_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case BQ_ERR_WORKSPACE: return "the workspace is NULL or smaller than bq_spec_verify_workspace reports";
@@ -293,6 +297,35 @@ int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* bias
   int st = validate(E_QMM, x, w, scales, biases, y, M, N, K, bits, group_size);
   if (st != BQ_OK) return st;
   return launch_qmm(x, w, scales, biases, y, M, N, K, BQ_BITS_T5, group_size, stream);
+}
+
+int bq_qmm_workspace(int M, int N, int K, int bits, int group_size, size_t* bytes) {
+  if (!bytes) return BQ_ERR_NULL;
+  *bytes = 0;
+  if (bits != 1 && bits != 2 && bits != BQ_BITS_T5) return BQ_ERR_BITS;
+  if (group_size != 64 && group_size != 128) return BQ_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % group_size != 0 || K > (1 << 26)) return BQ_ERR_SHAPE;
+  if (M < 1) return BQ_ERR_M;
+  if (M > 32) return BQ_OK;
+  const QmmSmallChoice c = qmm_small_m_choice(M, N, K, SIZE_MAX);
+  if (c.split > 1) *bytes = (size_t)c.split * qmm_part_stride(M, N) * sizeof(float);
+  return BQ_OK;
+}
+
+int bq_qmm_ws(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
+              int K, int bits, int group_size, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(E_UQMM, x, w, scales, biases, y, M, N, K, bits, group_size);
+  if (st != BQ_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return BQ_ERR_ALIGN;
+  return launch_qmm(x, w, scales, biases, y, M, N, K, bits, group_size, stream, workspace, workspace_bytes);
+}
+
+int bq_t5_qmm_ws(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
+                 int N, int K, int bits, int group_size, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate(E_QMM, x, w, scales, biases, y, M, N, K, bits, group_size);
+  if (st != BQ_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return BQ_ERR_ALIGN;
+  return launch_qmm(x, w, scales, biases, y, M, N, K, BQ_BITS_T5, group_size, stream, workspace, workspace_bytes);
 }
 
 int bq_dequant(const void* x, const void* w, const void* scales, const void* biases, void* y, int M,
@@ -379,6 +412,19 @@ int bq_linear(const void* x, const void* w, const void* scales, const void* bias
     if (st != BQ_OK) return st;
   }
   return BQ_OK;
+}
+
+int bq_linear_ws(const void* x, const void* w, const void* scales, const void* biases, void* y, int M, int N,
+                 int K, int bits, int group_size, int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags, stream);
+  if ((flags & ~BQ_LINEAR_SYM) != 0) return BQ_ERR_FLAGS;
+  const bool t5 = bits == BQ_BITS_T5;
+  if (M < (t5 ? BQ_T5_QMM_MIN_M : BQ_QMM_MIN_M))
+    return bq_linear(x, w, scales, biases, y, M, N, K, bits, group_size, flags, stream);
+  const void* b = (flags & BQ_LINEAR_SYM) ? nullptr : biases;
+  if (t5) return bq_t5_qmm_ws(x, w, scales, b, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream);
+  if (!b && !(flags & BQ_LINEAR_SYM)) return BQ_ERR_NULL;
+  return bq_qmm_ws(x, w, scales, b, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream);
 }
 
 int bq_sym_check(const void* scales, const void* biases, int N, int K, int bits, int group_size, int* flag,

@@ -59,7 +59,18 @@ struct QmmParams {
   half_t* y;           // [M][N]
   int M, N, K, G, row_bytes;
   int x_bytes, w_bytes, sb_bytes;  // buffer descriptor sizes
+  // K split (qmm_deep_kernel only): ksplit workgroups per tile, each over
+  // its share of the K iterations, storing fp32 partial tiles to part
+  // (ksplit slices of qmm_part_stride(M, N) floats, [M][N] each) instead
+  // of y (part == null: ksplit is 1, y direct)
+  float* part;
+  int ksplit;
+  size_t part_cap;  // host side: bytes the caller's workspace holds
 };
+
+// floats per partial-sum slice: M*N rounded up to a multiple of 4 (each
+// slice starts 16-byte aligned)
+__host__ __device__ inline size_t qmm_part_stride(int M, int N) { return ((size_t)M * N + 3) & ~(size_t)3; }
 
 constexpr int kQmmBK = 64;        // codes per K step
 constexpr int kQmmThreads = 512;  // 4 MFMA waves (2 x 2 over the tile) + 4 loading/decoding waves
@@ -584,10 +595,17 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
   const int pw = wave & 3;
   const int wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int t = (int)blockIdx.x;
+  // workgroup -> tile and K share: the ksplit shares of a tile are
+  // neighbours; share ks walks iterations [itb, itb + IT) (ksplit is at
+  // most the iteration count, so every share has one)
+  const int S = p.ksplit;
+  const int t = (int)blockIdx.x / S;
+  const int ks = (int)blockIdx.x - t * S;
   const int m0 = (t / tiles_n) * BM;
   const int n0 = (t % tiles_n) * BN;
-  const int IT = p.K / (kQmmBK * SUB);
+  const int IT_all = p.K / (kQmmBK * SUB);
+  const int itb = (int)((int64_t)ks * IT_all / S);
+  const int IT = (int)((int64_t)(ks + 1) * IT_all / S) - itb;
 
   // s_waitcnt lgkmcnt(0), the other counters free: this wave's LDS stores
   // are done (barriers here wait for nothing else)
@@ -607,10 +625,10 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
     Set set[D];
     // x unit c*64 + lane of a step buffer (c = i*4 + pw) holds row
     // (c*64+lane)/8 of the tile, 16-byte column q XOR row%8
-    auto issue = [&](int it, Set& st) {
+    auto issue = [&](int it, Set& st) {  // it: iteration of this share
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
-        const int k0 = (it * SUB + u) * kQmmBK;
+        const int k0 = ((itb + it) * SUB + u) * kQmmBK;
 #pragma unroll
         for (int i = 0; i < XU; ++i) {
           const int un = (i * 4 + pw) * 64 + lane;
@@ -618,7 +636,7 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
           const uint32_t off = 2u * ((uint32_t)(m0 + row) * (uint32_t)p.K + (uint32_t)(k0 + q * 8));
           st.x[u][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
         }
-        dec.issue(it * SUB + u, st.raw[u]);
+        dec.issue((itb + it) * SUB + u, st.raw[u]);
       }
     };
     auto put = [&](int it, int buf, const Set& st) {
@@ -633,7 +651,7 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
         // in flight, and the reuse would wait for that load
         keep_loaded(st.raw[u].d);
         uint32_t out[NC / 2];
-        dec.decode(it * SUB + u, st.raw[u], lut, out);
+        dec.decode((itb + it) * SUB + u, st.raw[u], lut, out);
         half_t* wb = ws + (buf * SUB + u) * BN * kQmmBK;
 #pragma unroll
         for (int q = 0; q < NC / 8; ++q)
@@ -747,8 +765,34 @@ __global__ __launch_bounds__(kQmmThreads) void qmm_deep_kernel(QmmParams p) {
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + v;
         const int n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
-        if (m < p.M && n < p.N) p.y[(size_t)m * p.N + n] = (half_t)acc[i][j][v];
+        if (m < p.M && n < p.N) {
+          if (p.part)
+            p.part[(size_t)ks * qmm_part_stride(p.M, p.N) + (size_t)m * p.N + n] = acc[i][j][v];
+          else
+            p.y[(size_t)m * p.N + n] = (half_t)acc[i][j][v];
+        }
       }
+}
+
+struct QmmSumParams {
+  const float* part;  // S slices of qmm_part_stride(M, N) floats, 16-byte aligned
+  half_t* y;          // [M][N]
+  size_t MN;          // M * N
+  int S;
+};
+
+// y[i] = fp16_rne(part[0][i] + part[1][i] + ... + part[S-1][i]), summed in
+// that order, V = 4 elements per thread
+template <int V>
+__global__ __launch_bounds__(256) void qmm_split_sum_kernel(QmmSumParams p) {
+  static_assert(V == 4, "one 16-byte vector of each slice per thread");
+  const size_t stride = (p.MN + 3) & ~(size_t)3;
+  const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * V;
+  if (i0 >= p.MN) return;
+  float4_t a = *reinterpret_cast<const float4_t*>(p.part + i0);
+  for (int k = 1; k < p.S; ++k) a += *reinterpret_cast<const float4_t*>(p.part + (size_t)k * stride + i0);
+  const int live = p.MN - i0 < V ? (int)(p.MN - i0) : V;
+  for (int e = 0; e < live; ++e) p.y[i0 + e] = (half_t)a[e];
 }
 
 }  // namespace bq

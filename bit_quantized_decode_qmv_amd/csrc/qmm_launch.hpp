@@ -29,7 +29,8 @@ int launch_qmm_s(const QmmParams& p, void* stream) {
   return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
 }
 
-// x and the raw weight bytes requested D iterations ahead into registers
+// x and the raw weight bytes requested D iterations ahead into registers;
+// p.ksplit workgroups per tile (p.part set when above 1)
 template <int BM, int BN, int BITS, int GS, bool IMPLIED, int SUB, int D>
 int launch_qmm_deep_s(const QmmParams& p, void* stream) {
   typedef QmmDecoder<BN, BITS, GS, IMPLIED> Dec;
@@ -37,9 +38,20 @@ int launch_qmm_deep_s(const QmmParams& p, void* stream) {
   const size_t lds = qmm_deep_lds_bytes(BM, BN, Dec::kLutWords, SUB);
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   (void)attr;
-  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
   QmmParams q = p;
-  return launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
+  // at most one share per K iteration, and only as many as the workspace holds
+  const int iters = p.K / (kQmmBK * SUB);
+  if (q.ksplit > iters) q.ksplit = iters;
+  if (q.ksplit < 1 || !q.part || (size_t)q.ksplit * qmm_part_stride(q.M, q.N) * sizeof(float) > q.part_cap)
+    q.ksplit = 1;
+  if (q.ksplit == 1) q.part = nullptr;
+  dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM) * q.ksplit);
+  int st = launch_kernel(fn, grid, dim3(kQmmThreads), lds, stream, &q);
+  if (st != BQ_OK || q.ksplit == 1) return st;
+  QmmSumParams sp{q.part, q.y, (size_t)q.M * q.N, q.ksplit};
+  const size_t vecs = (sp.MN + 3) / 4;
+  return launch_kernel(reinterpret_cast<const void*>(&qmm_split_sum_kernel<4>), dim3((unsigned)((vecs + 255) / 256)),
+                       dim3(256), 0, stream, &sp);
 }
 
 // Small products (M <= 32, 32-row tiles) request x and the weight bytes
@@ -50,52 +62,25 @@ int launch_qmm_deep_s(const QmmParams& p, void* stream) {
 constexpr int kQmmDepth = 4;
 constexpr int kQmmDepthWide = 2;
 
-// sub: K steps per iteration (4, 2 or 1), reduced to what divides the step
-// count (and to 2 for 128-column tiles: the LDS of their double buffers)
-template <int BN, int BITS, int GS, bool IMPLIED>
-int launch_qmm_deep_t(const QmmParams& p, int sub, void* stream) {
-  const int steps = p.K / kQmmBK;
-  if (BN == 64 && sub >= 4 && steps % 4 == 0)
-    return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, (BN == 64 ? 4 : 2), kQmmDepth>(p, stream);
-  if (sub >= 2 && steps % 2 == 0) return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, 2, kQmmDepth>(p, stream);
-  return launch_qmm_deep_s<32, BN, BITS, GS, IMPLIED, 1, kQmmDepth>(p, stream);
-}
-
-// Small products (M <= 32, only 32-row tiles) are bound by the time of one
-// pipeline iteration, not by the MFMA or memory throughput.  Measured on
-// MI355X at M = 32 with one iteration of prefetch, an iteration of SUB steps
-// took about 0.57 us plus 0.43 us per step with 64-column tiles and 0.50 us
-// per step with 128-column tiles; the deeper prefetch now used cuts both
-// by about a third and keeps their order, which is all the choice below
-// uses.  Estimated microseconds of (BN, SUB) over `tiles` workgroups (two
-// per CU only for 32 x 64 tiles without SUB, whose LDS allows it).
-double qmm_small_m_us(int tiles, int steps, int BN, int sub) {
-  const int per_cu = (BN == 64 && sub == 1) ? 2 : 1;
-  const double rounds = std::ceil((double)tiles / (256.0 * per_cu));
-  const double iter = 0.57 + sub * (BN == 64 ? 0.43 : 0.50);
-  return rounds * ((double)steps / sub) * iter;
+// the small-M product as qmm_small_m_choice picks it (split 1 without a
+// workspace)
+template <int BITS, int GS, bool IMPLIED>
+int launch_qmm_small(const QmmParams& p, void* stream) {
+  const QmmSmallChoice c = qmm_small_m_choice(p.M, p.N, p.K, p.part ? p.part_cap : 0);
+  QmmParams q = p;
+  q.ksplit = c.split;
+  constexpr int D = kQmmDepth;
+  if (c.bn == 64)
+    return c.sub == 4 ? launch_qmm_deep_s<32, 64, BITS, GS, IMPLIED, 4, D>(q, stream)
+                      : launch_qmm_deep_s<32, 64, BITS, GS, IMPLIED, 1, D>(q, stream);
+  return c.sub == 2 ? launch_qmm_deep_s<32, 128, BITS, GS, IMPLIED, 2, D>(q, stream)
+                    : launch_qmm_deep_s<32, 128, BITS, GS, IMPLIED, 1, D>(q, stream);
 }
 
 template <int BITS, int GS, bool IMPLIED>
 int launch_qmm_m(const QmmParams& p, void* stream) {
   const int steps = p.K / kQmmBK;
-  if (p.M <= 32) {
-    // 32 x 64 (SUB 1 or 4) or 32 x 128 (SUB 1 or 2), whichever the measured
-    // iteration times say is shortest
-    const int t64 = (p.N + 63) / 64, t128 = (p.N + 127) / 128;
-    struct Opt {
-      int bn, sub;
-      double us;
-    } opts[] = {{64, 1, qmm_small_m_us(t64, steps, 64, 1)},
-                {64, 4, steps % 4 == 0 ? qmm_small_m_us(t64, steps, 64, 4) : 1e30},
-                {128, 1, qmm_small_m_us(t128, steps, 128, 1)},
-                {128, 2, steps % 2 == 0 ? qmm_small_m_us(t128, steps, 128, 2) : 1e30}};
-    const Opt* o = &opts[0];
-    for (const Opt& c : opts)
-      if (c.us < o->us) o = &c;
-    return o->bn == 64 ? launch_qmm_deep_t<64, BITS, GS, IMPLIED>(p, o->sub, stream)
-                       : launch_qmm_deep_t<128, BITS, GS, IMPLIED>(p, o->sub, stream);
-  }
+  if (p.M <= 32) return launch_qmm_small<BITS, GS, IMPLIED>(p, stream);
   // Rules from a measured sweep of seven tiles and prefetch depths 1-4
   // (MI355X; q 6144 x 5120, gate 17408 x 5120, down 5120 x 17408; t5 and
   // 2-bit; M 64 .. 2048), in microseconds per call:

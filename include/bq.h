@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 8
+#define BQ_ABI_VERSION 9
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -165,6 +165,35 @@ int bq_t5_qmm(const void* x, const void* w, const void* scales, const void* bias
 int bq_qmm(const void* x, const void* w, const void* scales, const void* biases, void* y,
            int M, int N, int K, int bits, int group_size, void* stream);
 
+/* K-split prefill -- section 二 path 3 (and path 1 for bits 1/2): the
+ * products of bq_t5_qmm and bq_qmm with a caller-owned workspace.  At most
+ * 32 rows give few output tiles (a 5120-column product has 80) for the
+ * 256 CUs, so the K iterations of each tile are shared by up to 8
+ * workgroups: each stores its fp32 partial tile to the workspace and a
+ * second kernel adds the partials in a fixed order (same result every
+ * call) and rounds once to fp16.  The sum order differs from the unsplit
+ * product, so results may differ from bq_t5_qmm / bq_qmm in the last
+ * bits (both are within the decode tolerance of the exact product).
+ *
+ * bq_qmm_workspace: *bytes := the workspace the split the library would
+ * choose for (M, N, K, bits, group_size) needs; 0 when it would not split
+ * (M > 32, or enough tiles).  bits 1, 2 or BQ_BITS_T5.  Host-only.
+ *
+ * bq_t5_qmm_ws / bq_qmm_ws: arguments as bq_t5_qmm / bq_qmm, plus
+ * workspace (device memory, 16-byte aligned, or NULL) of workspace_bytes
+ * bytes.  The split is taken only as far as the workspace holds its
+ * partials; NULL or too small a workspace gives the unsplit product (no
+ * error).  The workspace needs no initial contents; concurrent calls on
+ * different streams must not share one.  BQ_ERR_ALIGN for a misaligned
+ * workspace, else the errors of bq_t5_qmm / bq_qmm. */
+int bq_qmm_workspace(int M, int N, int K, int bits, int group_size, size_t* bytes);
+int bq_t5_qmm_ws(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                 int M, int N, int K, int bits, int group_size, void* workspace, size_t workspace_bytes,
+                 void* stream);
+int bq_qmm_ws(const void* x, const void* w, const void* scales, const void* biases, void* y,
+              int M, int N, int K, int bits, int group_size, void* workspace, size_t workspace_bytes,
+              void* stream);
+
 /* dequant -- section 二 path 1 (1-bit prefill dequantizes to float16
  * before a matmul): y := fp16 [N][K], y[n][k] = fp16_rne(scale*q + bias)
  * computed exactly and rounded once.  x is ignored (may be NULL) and so is
@@ -191,6 +220,19 @@ int bq_dequant(const void* x, const void* w, const void* scales, const void* bia
  * anything runs.  Undefined flag bits: BQ_ERR_FLAGS. */
 int bq_linear(const void* x, const void* w, const void* scales, const void* biases, void* y,
               int M, int N, int K, int bits, int group_size, int flags, void* stream);
+
+/* linear with a workspace -- the routing of bq_linear, where a
+ * workspace lets the fused prefill product split K (bq_t5_qmm_ws /
+ * bq_qmm_ws): from BQ_T5_QMM_MIN_M (t5) or BQ_QMM_MIN_M (bits 1/2) rows
+ * every product takes the fused route whatever its tile count, with
+ * the workspace; fewer rows take the passes of bq_linear.  workspace ==
+ * NULL: exactly bq_linear.  The fused route needs bq_qmm_workspace bytes
+ * for its full split (less: a smaller split or none, see bq_qmm_ws);
+ * workspace 16-byte aligned.  Arguments and errors otherwise as
+ * bq_linear. */
+int bq_linear_ws(const void* x, const void* w, const void* scales, const void* biases, void* y,
+                 int M, int N, int K, int bits, int group_size, int flags, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* The route bq_linear takes for (M, N, bits, flags), a bq_route value, and
  * the number of kernel passes in *passes (may be NULL); BQ_ERR_M,

@@ -32,7 +32,7 @@ class _NoLaunch:
     def __getattr__(self, name):
         fn = getattr(self._lib, name)
         if not name.startswith("bq_") or name in ("bq_abi_version", "bq_strerror", "bq_linear_route",
-                                                  "bq_spec_verify_workspace"):
+                                                  "bq_spec_verify_workspace", "bq_qmm_workspace"):
             return fn
 
         def checked(*args):
@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 8
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 9
 
 
 def test_strerror_covers_every_status(lib):
@@ -189,6 +189,72 @@ def test_decode_dword_alignment(lib, name):
     assert call(lib, name, bits=bits, s=PS + 2) == ALIGN
     if name != "bq_qmv_sym":  # sym never reads the bias pointer
         assert call(lib, name, bits=bits, b=PB + 2) == ALIGN
+
+
+PWS = 6 * P  # fake workspace
+
+
+def call_ws(lib, name, ws=PWS, ws_bytes=1 << 24, **kw):
+    x, w, sc, b, y = (kw.pop(k, d) for k, d in (("x", PX), ("w", PW), ("s", PS), ("b", PB), ("y", PY)))
+    M, N, K, bits, gs = (kw.pop(k, d) for k, d in (("M", 1), ("N", 8), ("K", 256), ("bits", 2), ("gs", 64)))
+    assert not kw
+    return getattr(lib, name)(x, w, sc, b, y, M, N, K, bits, gs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,bits", [("bq_t5_qmm_ws", 0), ("bq_qmm_ws", 2)])
+def test_split_prefill_entries_validate(lib, name, bits):
+    """The K-split products check the arguments of bq_t5_qmm / bq_qmm, then
+    a 16-byte aligned workspace, before any launch."""
+    for kw in ("w", "s", "y", "x"):
+        assert call_ws(lib, name, bits=bits, **{kw: None}) == NULL
+    assert call_ws(lib, name, bits=1 if bits == 0 else 0) == BITS
+    assert call_ws(lib, name, bits=bits, gs=96) == GROUP
+    assert call_ws(lib, name, bits=bits, K=320, gs=128) == SHAPE
+    assert call_ws(lib, name, bits=bits, M=0) == MRANGE
+    assert call_ws(lib, name, bits=bits, x=PX + 8) == ALIGN
+    assert call_ws(lib, name, bits=bits, y=PY + 1) == ALIGN
+    for off in (4, 8, 12):
+        assert call_ws(lib, name, bits=bits, ws=PWS + off) == ALIGN
+
+
+def test_linear_ws_validates(lib):
+    def lw(flags=0, ws=PWS, M=20, bits=0, **kw):
+        x, w, sc, b, y = (kw.pop(k, d) for k, d in (("x", PX), ("w", PW), ("s", PS), ("b", PB), ("y", PY)))
+        return lib.bq_linear_ws(x, w, sc, b, y, M, 8, 256, bits, 64, flags, ws, 1 << 20, None)
+    assert lw(flags=4) == -8  # BQ_ERR_FLAGS
+    assert lw(ws=PWS + 8) == ALIGN  # prefill rows: the split product checks its workspace
+    assert lw(w=None) == NULL
+    assert lw(bits=2, b=None) == NULL  # stored biases required without the symmetric flag
+    assert lw(bits=2, x=PX + 8) == ALIGN
+    assert lw(M=0) == MRANGE
+    assert lw(M=3, ws=PWS + 8, y=PY + 1) == ALIGN  # decode rows: bq_linear's checks
+    assert lw(M=3, bits=3) == BITS
+
+
+def test_split_prefill_workspace_size(lib):
+    import ctypes
+    n = ctypes.c_size_t(7)
+
+    def ws(M, N, K, bits=0, gs=128):
+        assert lib.bq_qmm_workspace(M, N, K, bits, gs, ctypes.byref(n)) == OK
+        return n.value
+
+    slice_ = lambda M, N: (M * N + 3) // 4 * 4 * 4
+    # few tiles (5120 columns: 80 of 64) at M <= 32: a split of 2..8 shares
+    for M, N in ((32, 5120), (17, 5120), (1, 1024), (5, 333)):
+        b = ws(M, N, 17408)
+        assert b % slice_(M, N) == 0 and 2 <= b // slice_(M, N) <= 8, (M, N, b)
+    assert ws(17, 1000, 2560, bits=2, gs=64) % slice_(17, 1000) == 0
+    # no split above 32 rows, nor where one K iteration leaves nothing to share
+    assert ws(33, 5120, 17408) == 0
+    assert ws(32, 5120, 64, bits=1, gs=64) == 0
+    assert bq.bq_qmm_workspace(32, 5120, 17408, 0, 128) == ws(32, 5120, 17408)
+    assert lib.bq_qmm_workspace(32, 8, 256, 3, 64, ctypes.byref(n)) == BITS
+    assert lib.bq_qmm_workspace(32, 8, 256, 2, 96, ctypes.byref(n)) == GROUP
+    assert lib.bq_qmm_workspace(32, 8, 320, 2, 128, ctypes.byref(n)) == SHAPE
+    assert lib.bq_qmm_workspace(32, 0, 256, 2, 64, ctypes.byref(n)) == SHAPE
+    assert lib.bq_qmm_workspace(0, 8, 256, 2, 64, ctypes.byref(n)) == MRANGE
+    assert lib.bq_qmm_workspace(1, 8, 256, 2, 64, None) == NULL
 
 
 def test_binding_raises_with_status(lib):

@@ -193,3 +193,42 @@ def test_linear_t5_prefill_routes(gs, M, NN):
         ref = np.concatenate([to_np(bq.t5_qmv_wide(x[m0:m0 + 5].contiguous(), qw.w, qw.scales, gs))
                               for m0 in range(0, M, 5)])
     assert np.array_equal(y.view(np.uint16), ref.view(np.uint16)), route
+
+
+# With a workspace (bq_linear_ws) the fused product takes every call from
+# the prefill row count on, whatever its tile count (its K split keeps few
+# tiles fast): 1024 columns are 16 tiles, which bq_linear sends to passes.
+@pytest.mark.parametrize("fmt,variant,sym", [("t5", "t5", False), ("u2", "asym", False), ("u1", "sym", True)])
+@pytest.mark.parametrize("M", [5, 16, 17, 32])
+def test_linear_ws_routes(fmt, variant, sym, M):
+    bq, torch = _bq()
+    NN, KK, gs = 1024, 2560, 64
+    inp = make(fmt, M, NN, KK, gs, variant)
+    qw = _qw(bq, inp)
+    x = dev(inp.x)
+    bits = {"u1": 1, "u2": 2, "t5": 0}[fmt]
+    need = bq.bq_qmm_workspace(M, NN, KK, bits, gs)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    y = to_np(bq.linear(x, qw, sym=sym, workspace=ws))
+    torch.cuda.synchronize()
+    assert_close(y.astype(np.float64), inp, what=f"linear_ws {fmt} M{M}")
+    prefill = M >= (bq.T5_QMM_MIN_M if fmt == "t5" else bq.QMM_MIN_M)
+    if prefill:
+        b = None if sym else qw.biases
+        want = (bq.t5_qmm_ws(x, qw.w, qw.scales, gs, biases=b, workspace=ws) if fmt == "t5"
+                else bq.qmm_ws(x, qw.w, qw.scales, bits, gs, biases=b, workspace=ws))
+    else:
+        want = bq.linear(x, qw, sym=sym)
+    assert np.array_equal(y.view(np.uint16), to_np(want).view(np.uint16))
+    # no workspace: exactly bq_linear
+    y0 = to_np(bq.linear(x, qw, sym=sym))
+    yn = torch.empty((M, NN), dtype=torch.float16, device="cuda:0")
+    bq.bq_linear_ws(x.data_ptr(), qw.w.data_ptr(), qw.scales.data_ptr(),
+                    qw.biases.data_ptr() if qw.biases is not None else None, yn.data_ptr(), M, NN, KK, bits, gs,
+                    bq.LINEAR_SYM if sym else 0, None, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(yn).view(np.uint16), y0.view(np.uint16))
+    # the binding's own workspace gives the same bits
+    ya = to_np(bq.linear(x, qw, sym=sym, workspace="auto"))
+    assert np.array_equal(ya.view(np.uint16), y.view(np.uint16))
