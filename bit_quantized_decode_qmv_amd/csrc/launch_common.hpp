@@ -46,7 +46,6 @@ QmvLauncher pick_qmv_t5(int gs, int M, bool implied);
 struct QmmSmallChoice {
   int bn, sub, split;
 };
-constexpr int kQmmMaxSplit = 8;
 
 // Unsplit: measured on MI355X at M = 32 with one iteration of prefetch, an
 // iteration of SUB steps took about 0.57 us plus 0.43 us per step with

@@ -781,18 +781,31 @@ struct QmmSumParams {
   int S;
 };
 
+constexpr int kQmmMaxSplit = 8;  // K shares per tile, at most
+
 // y[i] = fp16_rne(part[0][i] + part[1][i] + ... + part[S-1][i]), summed in
-// that order, V = 4 elements per thread
+// that order, V = 4 elements per thread.  The loads of all slices go out
+// before the first add, as straight-line code: slices past S reload slice
+// 0 (in bounds, not added).
 template <int V>
 __global__ __launch_bounds__(256) void qmm_split_sum_kernel(QmmSumParams p) {
   static_assert(V == 4, "one 16-byte vector of each slice per thread");
   const size_t stride = (p.MN + 3) & ~(size_t)3;
   const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * V;
   if (i0 >= p.MN) return;
-  float4_t a = *reinterpret_cast<const float4_t*>(p.part + i0);
-  for (int k = 1; k < p.S; ++k) a += *reinterpret_cast<const float4_t*>(p.part + (size_t)k * stride + i0);
-  const int live = p.MN - i0 < V ? (int)(p.MN - i0) : V;
-  for (int e = 0; e < live; ++e) p.y[i0 + e] = (half_t)a[e];
+  float4_t v[kQmmMaxSplit];
+#pragma unroll
+  for (int k = 0; k < kQmmMaxSplit; ++k)
+    v[k] = *reinterpret_cast<const float4_t*>(p.part + (size_t)(k < p.S ? k : 0) * stride + i0);
+  float4_t a = v[0];
+#pragma unroll
+  for (int k = 1; k < kQmmMaxSplit; ++k) {
+    const float4_t b = a + v[k];
+    a = k < p.S ? b : a;
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+    if (i0 + e < p.MN) p.y[i0 + e] = (half_t)a[e];
 }
 
 }  // namespace bq
