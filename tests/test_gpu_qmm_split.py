@@ -145,3 +145,51 @@ def test_binding_allocates_the_workspace():
     y_c, _ = _split_call(inp)
     y_b = to_np(bq.qmm_ws(dev(inp.x), dev(inp.w), dev(inp.scales), 1, 64, biases=dev(inp.biases)))
     assert np.array_equal(y_c.view(np.uint16), y_b.view(np.uint16))
+
+
+def test_graph_replays_match_eager_calls():
+    """The split products (and decode calls beside them) captured in one
+    graph give the eager bits on every replay, with eager work and
+    synchronizations between the replays (the workspace is reused by
+    replays and eager calls alike)."""
+    import bit_quantized_decode_qmv_amd as bq
+    torch = torch_mod()
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    cases = [make("t5", 24, 1000, 2560, 128, "t5", seed=117), make("u2", 32, 700, 1280, 64, "asym", seed=118),
+             make("t5", 5, 1000, 2560, 64, "t5", seed=119), make("u2", 3, 700, 1280, 64, "asym", seed=120)]
+    ins = [(dev(c.x), dev(c.w), dev(c.scales), dev(c.biases)) for c in cases]
+    outs = [torch.zeros((c.M, c.N), dtype=torch.float16, device="cuda:0") for c in cases]
+    need = max(bq.bq_qmm_workspace(c.M, c.N, c.K, BITS[c.fmt], c.group_size) for c in cases[:2])
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+
+    def launch_all():
+        for c, (x, w, s, b), y in zip(cases, ins, outs):
+            args = (x.data_ptr(), w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None, y.data_ptr(),
+                    c.M, c.N, c.K, BITS[c.fmt], c.group_size)
+            if c.M > 5:
+                fn = bq.bq_t5_qmm_ws if c.fmt == "t5" else bq.bq_qmm_ws
+                fn(*args, ws.data_ptr(), need, stream())
+            else:
+                fn = bq.bq_t5_qmv_wide if c.fmt == "t5" else bq.bq_qmv_wide
+                fn(*args, stream())
+
+    launch_all()
+    torch.cuda.synchronize()
+    eager = [to_np(y).copy() for y in outs]
+    for c, y in zip(cases, eager):
+        assert_close(y.astype(np.float64), c, what=f"eager {c.fmt} M{c.M}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch_all()
+    for r in range(3):
+        for y in outs:
+            y.zero_()
+        launch_all()  # eager calls on the same workspace between replays
+        torch.cuda.synchronize()
+        for y in outs:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, y, e in zip(cases, outs, eager):
+            assert np.array_equal(to_np(y).view(np.uint16), e.view(np.uint16)), f"replay {r}: {c.fmt} M{c.M}"
