@@ -399,6 +399,18 @@ def launch_set_run(torch, lib, dev, name):
         labels.append(f"{entry}/{fmt}-{variant}/gs{gs}/M{M}/{shape}")
         nbytes.append(nb)
         del x, w, s, b
+    if name == "dequant":
+        # reference for the write-bound dequant: a plain fill of the same
+        # fp16 [N][K] output (gate), after the same cache-evicting pass
+        N, K = synth.PROJECTION_SHAPES["gate"]
+        y = torch.empty((N, K), dtype=torch.float16, device=dev)
+        torch.add(dst, 1.0, out=src)
+        torch.cuda.synchronize()
+        y.fill_(1.0)
+        torch.cuda.synchronize()
+        labels.append("fill/gate")
+        nbytes.append(N * K * 2)
+        del y
     print(json.dumps({"launch_set": name, "calls": labels, "bytes": nbytes}), flush=True)
 
 
