@@ -49,7 +49,6 @@ Other modes:
 from __future__ import annotations
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -139,6 +138,13 @@ class Call:
                      y.data_ptr())
         self.bits = {"u1": 1, "u2": 2, "t5": 0}[fmt]
         self.bytes = algorithmic_bytes(fmt, M, N, K, gs, b is not None and entry != "bq_qmv_sym")
+        self.ws = None
+        if entry.endswith("_ws"):
+            # the K-split prefill products: a zero-filled workspace of the
+            # size the library asks for (shared by this call's copies)
+            import bit_quantized_decode_qmv_amd as bq
+            need = bq.bq_qmm_workspace(M, N, K, self.bits, gs)
+            self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=w.device)
 
     @property
     def y(self):
@@ -146,7 +152,11 @@ class Call:
 
     def launch(self, lib, stream):
         x, w, s, b, y = self.ptrs
-        st = getattr(lib, self.entry)(x, w, s, b, y, self.M, self.N, self.K, self.bits, self.gs, stream)
+        if self.ws is not None:
+            st = getattr(lib, self.entry)(x, w, s, b, y, self.M, self.N, self.K, self.bits, self.gs,
+                                          self.ws.data_ptr(), self.ws.numel(), stream)
+        else:
+            st = getattr(lib, self.entry)(x, w, s, b, y, self.M, self.N, self.K, self.bits, self.gs, stream)
         if st != 0:
             raise RuntimeError(f"{self.entry} {self.label}: status {st}")
 
@@ -158,6 +168,8 @@ class Call:
             ts = [t.clone() if t is not None else None for t in (x, w, s, b)]
             out.append(Call(torch, self.entry, self.fmt, self.variant, self.M, self.N, self.K, self.gs, ts,
                             self.label))
+            if self.ws is not None:
+                out[-1].ws = self.ws
         return out
 
 
@@ -379,15 +391,6 @@ def launch_set_run(torch, lib, dev, name):
             st = lib.bq_dequant(None, w.data_ptr(), s.data_ptr(), b.data_ptr() if b is not None else None,
                                 y.data_ptr(), 0, N, K, inp.bits, gs, h)
             nb = w.numel() * w.element_size() + s.numel() * 2 * (2 if b is not None else 1) + N * K * 2
-        elif entry == "bq_t5_qmm_ws":
-            # the K-split product: its kernel and the partial-sum kernel
-            c = Call(torch, "bq_t5_qmm", fmt, variant, M, N, K, gs, (x, w, s, b), "")
-            need = ctypes.c_size_t(0)
-            st = lib.bq_qmm_workspace(M, N, K, inp.bits, gs, ctypes.byref(need))
-            ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
-            px, pw, ps, pb, py = c.ptrs
-            st = st or lib.bq_t5_qmm_ws(px, pw, ps, pb, py, M, N, K, inp.bits, gs, ws.data_ptr(), need.value, h)
-            nb = c.bytes
         else:
             c = Call(torch, entry, fmt, variant, M, N, K, gs, (x, w, s, b), "")
             st = 0
@@ -490,6 +493,10 @@ def full_suite(torch, lib, dev, path):
             specs.append(("bq_t5_qmm", "t5", "t5", M, shape, 128))
             for fmt in ("u1", "u2"):
                 specs.append(("bq_qmm", fmt, "asym", M, shape, 128))
+    for M in (17, 32):  # the K-split products
+        for shape in SHAPES:
+            specs.append(("bq_t5_qmm_ws", "t5", "t5", M, shape, 128))
+            specs.append(("bq_qmm_ws", "u2", "asym", M, shape, 128))
     rows = []
     with open(path, "w") as f:
         f.write("entry,fmt,variant,M,shape,N,K,gs,us,GBps,frac_hbm,TFLOPs\n")
@@ -498,7 +505,7 @@ def full_suite(torch, lib, dev, path):
             inp = synth.make_inputs(fmt, M, N, K, gs, variant, seed=0)
             c = Call(torch, entry, fmt, variant, M, N, K, gs,
                      [upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)], "")
-            mm = entry in ("bq_t5_qmm", "bq_qmm")
+            mm = entry in ("bq_t5_qmm", "bq_qmm", "bq_t5_qmm_ws", "bq_qmm_ws")
             t = per_call_seconds(torch, lib, c, launches=8 if mm and M >= 512 else 40, replays=3)
             gbs = c.bytes / t / 1e9
             tflops = (2.0 * M * N * K / t / 1e12) if mm else 0.0
@@ -568,7 +575,6 @@ def spec_and_repack_rows(torch, lib, dev):
     import numpy as np
     import synth
     out = []
-    stream = torch.cuda.current_stream().cuda_stream
     for B, L in ((1, 4), (8, 4), (8, 7)):
         V = synth.QWEN_VOCAB
         s = synth.make_spec_inputs(B, L, V, dtype=np.float16, seed=0)
@@ -580,15 +586,17 @@ def spec_and_repack_rows(torch, lib, dev):
         a = torch.empty(B, dtype=torch.int32, device=dev)
         nx = torch.empty(B, dtype=torch.int32, device=dev)
 
-        def one():
+        def one(h):
             st = lib.bq_spec_decode_verify(lg.data_ptr(), 1, dr.data_ptr(), B, L, V, a.data_ptr(), nx.data_ptr(),
-                                           None, ws.data_ptr(), n.value, stream)
+                                           None, ws.data_ptr(), n.value, h)
             if st != 0:
                 raise RuntimeError(f"bq_spec_decode_verify: status {st}")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
+            # the capturing stream (the graph context makes it current)
+            hs = torch.cuda.current_stream().cuda_stream
             for _ in range(20):
-                one()
+                one(hs)
         g.replay()
         t = time_graphs(torch, [g], 5) / 100
         nbytes = B * (L + 1) * V * 2
@@ -602,8 +610,11 @@ def spec_and_repack_rows(torch, lib, dev):
     flag = torch.empty(1, dtype=torch.int32, device=dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        hs = torch.cuda.current_stream().cuda_stream
         for _ in range(10):
-            lib.bq_t5_repack(w.data_ptr(), o.data_ptr(), N, K, 2, 128, flag.data_ptr(), stream)
+            st = lib.bq_t5_repack(w.data_ptr(), o.data_ptr(), N, K, 2, 128, flag.data_ptr(), hs)
+            if st != 0:
+                raise RuntimeError(f"bq_t5_repack: status {st}")
     g.replay()
     t = time_graphs(torch, [g], 3) / 30
     nbytes = w.numel() * 4 + o.numel()

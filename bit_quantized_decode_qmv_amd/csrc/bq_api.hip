@@ -458,8 +458,8 @@ int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_si
   p.w = static_cast<const uint32_t*>(w);
   p.out = static_cast<uint32_t*>(w_t5);
   p.words_per_row = K / 32 * bits;
-  p.dwords_per_row = row_bytes_of(BQ_BITS_T5, K, group_size) / 4;
-  p.total = (int64_t)N * p.dwords_per_row;
+  p.groups_per_row = K / group_size;
+  p.groups = (int64_t)N * p.groups_per_row;
   p.flag = flag;
   int st = launch(reinterpret_cast<const void*>(&repack_flag_init_kernel), dim3(1), dim3(64), 0, stream, &p);
   if (st != BQ_OK) return st;
@@ -471,7 +471,8 @@ int bq_t5_repack(const void* w, void* w_t5, int N, int K, int bits, int group_si
     fn = group_size == 64 ? reinterpret_cast<const void*>(&t5_repack_kernel<2, 64>)
                           : reinterpret_cast<const void*>(&t5_repack_kernel<2, 128>);
   }
-  const int64_t blocks = std::min<int64_t>((p.total + 255) / 256, 8192);
+  const int64_t blocks = (p.groups + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return BQ_ERR_SHAPE;
   return launch(fn, dim3((unsigned)blocks), dim3(256), 0, stream, &p);
 }
 

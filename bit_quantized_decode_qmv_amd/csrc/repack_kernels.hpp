@@ -8,8 +8,10 @@
 //
 // Layout written: t5 row n is (K/gs) groups of ceil(gs/5) bytes; code 5j+i
 // of a group is digit i (least significant first) of the group's byte j,
-// unused digits 0.  One thread per output dword: its four bytes take twenty
-// codes, read from the row's uint32 words (LSB-first codes).
+// unused digits 0.  One thread per group: it loads the group's code words
+// (2 to 8 dwords), forms the group's 13 or 26 bytes in registers, and the
+// workgroup's 256 groups -- a contiguous, dword-aligned run of output bytes
+// when K is a multiple of 256 -- go out through LDS as whole dwords.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,8 +22,8 @@ namespace bq {
 struct RepackParams {
   const uint32_t* w;  // [N][words_per_row] 1/2-bit codes
   uint32_t* out;      // [N][dwords_per_row] t5 bytes
-  int64_t total;      // N * dwords_per_row
-  int words_per_row, dwords_per_row;
+  int64_t groups;     // N * (K / gs)
+  int words_per_row, groups_per_row;
   int* flag;          // 1 = every code was 0..2, 0 = a code 3 was met
 };
 
@@ -31,35 +33,44 @@ __global__ void repack_flag_init_kernel(RepackParams p) {
 
 template <int BITS, int GS>
 __global__ __launch_bounds__(256) void t5_repack_kernel(RepackParams p) {
-  constexpr int GB = (GS + 4) / 5;  // bytes per group
+  constexpr int GB = (GS + 4) / 5;        // bytes per group
+  constexpr int NW = GS * BITS / 32;      // code words per group
   constexpr uint32_t kMask = (1u << BITS) - 1u;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[256 * GB];
+  const int64_t q0 = (int64_t)blockIdx.x * 256;
+  const int64_t q = q0 + threadIdx.x;
+  const int nlive = (int)(p.groups - q0 < 256 ? p.groups - q0 : 256);
   bool ternary = true;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.total; i += stride) {
-    const int n = (int)(i / p.dwords_per_row);
-    const int d = (int)(i - (int64_t)n * p.dwords_per_row);
-    const uint32_t* row = p.w + (size_t)n * p.words_per_row;
-    uint32_t v = 0;
+  if (q < p.groups) {
+    const int n = (int)(q / p.groups_per_row);
+    const int g = (int)(q - (int64_t)n * p.groups_per_row);
+    const uint32_t* src = p.w + (size_t)n * p.words_per_row + (size_t)g * NW;
+    uint32_t wd[NW];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int b = 4 * d + e;  // byte within the row
-      const int g = b / GB, j = b - g * GB;
+    for (int i = 0; i < NW; ++i) wd[i] = src[i];
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
       uint32_t byte = 0, pw = 1;
 #pragma unroll
       for (int t = 0; t < 5; ++t) {
         const int c = 5 * j + t;  // code within the group
         if (c < GS) {
-          const int k = g * GS + c;
-          const uint32_t q = (row[(k * BITS) >> 5] >> ((k * BITS) & 31)) & kMask;
-          ternary = ternary && q <= 2u;
-          byte += (q > 2u ? 2u : q) * pw;
+          const uint32_t qc = (wd[(c * BITS) >> 5] >> ((c * BITS) & 31)) & kMask;
+          ternary = ternary && qc <= 2u;
+          byte += (qc > 2u ? 2u : qc) * pw;
         }
         pw *= 3u;
       }
-      v |= byte << (8 * e);
+      stage[threadIdx.x * GB + j] = (uint8_t)byte;
     }
-    p.out[i] = v;
   }
+  __syncthreads();
+  // the live groups' bytes, nlive * GB of them (a multiple of 4: rows hold
+  // a multiple of 4 groups of 13 bytes or 2 of 26), as dwords
+  const uint32_t* st = reinterpret_cast<const uint32_t*>(stage);
+  uint32_t* dst = p.out + q0 * GB / 4;
+  const int ndw = nlive * GB / 4;
+  for (int i = (int)threadIdx.x; i < ndw; i += 256) dst[i] = st[i];
   if (!ternary) *p.flag = 0;
 }
 

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bq.h"
+
 namespace bq {
 
 constexpr int kSpecChunk = 8192;   // logits per workgroup
@@ -71,15 +73,32 @@ __global__ __launch_bounds__(kSpecThreads) void spec_verify_kernel(SpecParams p)
   const int v1 = min(v0 + kSpecChunk, p.V);
   const T* lg = static_cast<const T*>(p.logits) + ((size_t)b * rows + row) * (size_t)p.V;
 
-  // chunk maximum: consecutive threads read consecutive values
-  unsigned long long best = 0;
-  for (int v = v0 + (int)threadIdx.x; v < v1; v += kSpecThreads) {
-    uint32_t k;
-    if constexpr (sizeof(T) == 2) k = spec_key(__builtin_bit_cast(uint16_t, lg[v]));
-    else k = spec_key(lg[v]);
-    const unsigned long long c = spec_pack(k, v);
-    best = c > best ? c : best;
+  // chunk maximum: consecutive threads read consecutive values (a wave
+  // instruction reads 64 consecutive values); all of a thread's loads are
+  // issued before the first comparison, and a thread keeps its largest key
+  // with the first index that has it (its values come in increasing v)
+  constexpr int NL = kSpecChunk / kSpecThreads;
+  T val[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int v = v0 + j * kSpecThreads + (int)threadIdx.x;
+    val[j] = v < v1 ? lg[v] : T(0);
   }
+  uint32_t bk = 0;
+  int bv = v0;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int v = v0 + j * kSpecThreads + (int)threadIdx.x;
+    uint32_t k;
+    if constexpr (sizeof(T) == 2) k = spec_key(__builtin_bit_cast(uint16_t, val[j]));
+    else k = spec_key(val[j]);
+    k = v < v1 ? k : 0u;
+    if (k > bk) {
+      bk = k;
+      bv = v;
+    }
+  }
+  unsigned long long best = bk ? spec_pack(bk, bv) : 0ull;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long c = __shfl_xor(best, o, 64);
@@ -91,31 +110,42 @@ __global__ __launch_bounds__(kSpecThreads) void spec_verify_kernel(SpecParams p)
     unsigned long long m = red[0];
 #pragma unroll
     for (int w = 1; w < kSpecThreads / 64; ++w) m = red[w] > m ? red[w] : m;
-    atomicMax(&p.keys[(size_t)b * rows + row], m);
-    __threadfence();
-    const unsigned int done = atomicAdd(&p.counters[b], 1u);
+    // the row's key, then the count: the count is taken only after the max
+    // has returned, i.e. has been performed where device-scope atomics are
+    // (a device-scope fence here would write back and invalidate this XCD's
+    // L2 once per workgroup, which dominated the call's time)
+    const unsigned long long old =
+        __hip_atomic_fetch_max(&p.keys[(size_t)b * rows + row], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(old) : "memory");
+    const unsigned int done = __hip_atomic_fetch_add(&p.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = done == (unsigned int)(rows * p.chunks - 1);
   }
   __syncthreads();
   if (!last) return;
-  // the last workgroup of sequence b: every row key is final
-  __threadfence();
+  // the last workgroup of sequence b: every row key is final (each was
+  // performed before its count, and the keys are read with device-scope
+  // atomic loads).  Its threads take the rows in parallel (one round trip
+  // per row, not one per row in sequence): each reads its row's key, writes
+  // the target token, notes a draft mismatch, and clears the key.
+  __shared__ int tl[BQ_SPEC_MAX_DRAFT + 1];
+  __shared__ int first_bad;
+  if (threadIdx.x == 0) first_bad = p.L;
+  __syncthreads();
+  unsigned long long* keys = p.keys + (size_t)b * rows;
+  for (int i = (int)threadIdx.x; i < rows; i += kSpecThreads) {
+    const unsigned long long k = __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int t = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+    tl[i] = t;
+    if (p.target) p.target[(size_t)b * rows + i] = t;
+    if (i < p.L && p.draft[(size_t)b * p.L + i] != t) atomicMin(&first_bad, i);
+    __hip_atomic_store(&keys[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned long long* keys = p.keys + (size_t)b * rows;
-    int a = p.L, next = -1;
-    for (int i = 0; i < rows; ++i) {
-      const unsigned long long k = atomicAdd(&keys[i], 0ull);  // coherent read
-      const int t = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-      if (p.target) p.target[(size_t)b * rows + i] = t;
-      if (next < 0 && (i == p.L || p.draft[(size_t)b * p.L + i] != t)) {
-        a = i;
-        next = t;
-      }
-      atomicExch(&keys[i], 0ull);
-    }
+    const int a = first_bad;
     p.accepted[b] = a;
-    p.next_token[b] = next;
-    atomicExch(&p.counters[b], 0u);
+    p.next_token[b] = tl[a];
+    __hip_atomic_store(&p.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
