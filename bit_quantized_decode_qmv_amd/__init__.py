@@ -23,7 +23,7 @@ import ctypes
 import os
 from typing import Optional
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 BITS_T5 = 0
 MAX_WIDE_M = 5
 LINEAR_SYM = 1

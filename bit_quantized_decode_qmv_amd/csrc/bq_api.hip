@@ -70,8 +70,6 @@ int validate(Entry e, const void* x, const void* w, const void* scales, const vo
 }
 
 // spec verify workspace: row keys, then per-sequence counters
-size_t spec_keys_bytes(int B, int L) { return ((size_t)B * (L + 1) * 8 + 255) / 256 * 256; }
-size_t spec_workspace_bytes(int B, int L) { return spec_keys_bytes(B, L) + (size_t)B * 4; }
 
 // Scratch of the allocation-free verify entry point: a file-scope device
 // array, one copy per GPU, held until the process ends.  Host code never
@@ -202,9 +200,8 @@ int spec_validate(const void* logits, int logits_dtype, const int* draft, int B,
   if (!logits || (L > 0 && !draft) || !accepted || !next_token) return BQ_ERR_NULL;
   if (logits_dtype != BQ_DTYPE_F16 && logits_dtype != BQ_DTYPE_F32) return BQ_ERR_BITS;
   if (B < 1 || L < 0 || L > BQ_SPEC_MAX_DRAFT || V < 1) return BQ_ERR_SHAPE;
-  const int64_t chunks = (V + kSpecChunk - 1) / kSpecChunk;
-  if ((int64_t)B * (L + 1) * chunks >= (1ll << 31)) return BQ_ERR_SHAPE;
   const size_t esz = logits_dtype == BQ_DTYPE_F16 ? 2 : 4;
+  if ((int64_t)B * (L + 1) * spec_chunks(V, (int)esz) >= (1ll << 31)) return BQ_ERR_SHAPE;
   if (!aligned(logits, esz) || (draft && !aligned(draft, 4)) || !aligned(accepted, 4) || !aligned(next_token, 4) ||
       (target_tokens && !aligned(target_tokens, 4)))
     return BQ_ERR_ALIGN;
@@ -220,11 +217,13 @@ int spec_launch(const void* logits, int logits_dtype, const int* draft, int B, i
   p.next_token = next_token;
   p.target = target_tokens;
   p.keys = static_cast<unsigned long long*>(workspace);
-  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + spec_keys_bytes(B, L));
+  char* ws = static_cast<char*>(workspace);
+  p.row_counts = reinterpret_cast<unsigned int*>(ws + spec_keys_bytes(B, L));
+  p.counters = reinterpret_cast<unsigned int*>(ws + spec_keys_bytes(B, L) + spec_row_counts_bytes(B, L));
   p.B = B;
   p.L = L;
   p.V = V;
-  p.chunks = (int)((V + kSpecChunk - 1) / kSpecChunk);
+  p.chunks = (int)spec_chunks(V, logits_dtype == BQ_DTYPE_F16 ? 2 : 4);
   const void* fn = logits_dtype == BQ_DTYPE_F16 ? reinterpret_cast<const void*>(&spec_verify_kernel<_Float16>)
                                                 : reinterpret_cast<const void*>(&spec_verify_kernel<float>);
   return launch(fn, dim3((unsigned)((int64_t)B * (L + 1) * p.chunks)), dim3(kSpecThreads), 0, stream, &p);

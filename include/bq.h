@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BQ_ABI_VERSION 9
+#define BQ_ABI_VERSION 10
 #define BQ_BITS_T5 0
 #define BQ_MAX_WIDE_M 5
 
@@ -302,12 +302,12 @@ int bq_spec_decode_verify(const void* logits, int logits_dtype, const int* draft
  * launches, no allocation of any kind.  A call whose scratch,
  * bq_spec_verify_workspace(B, L), exceeds the array returns BQ_ERR_SCRATCH
  * before launching anything (e.g. B = 256 sequences of L = 15 draft tokens
- * need about 33 KB).  Every call on a GPU shares that GPU's array: calls
+ * need about 1.1 MB: 256 bytes per verified position, 128 per sequence).  Every call on a GPU shares that GPU's array: calls
  * that overlap in time on one GPU (several streams, several host threads)
  * race and give wrong results; serialize them.  Other errors as
  * bq_spec_decode_verify; BQ_ERR_HIP if the array's address cannot be
  * taken. */
-#define BQ_SPEC_NOALLOC_SCRATCH_BYTES (256 * 1024)
+#define BQ_SPEC_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
 int bq_spec_decode_verify_noalloc(const void* logits, int logits_dtype, const int* draft, int B, int L, int V,
                                   int* accepted, int* next_token, int* target_tokens, void* stream);
 

@@ -66,7 +66,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bq_abi_version() == bq.ABI_VERSION == 9
+    assert lib.bq_abi_version() == bq.ABI_VERSION == 10
 
 
 def test_strerror_covers_every_status(lib):
@@ -457,8 +457,9 @@ def test_spec_verify_noalloc_validates(lib):
     assert sv(L=1025) == SHAPE
     assert sv(lg=PY + 1) == ALIGN
     assert sv(t=T + 2) == ALIGN
-    # scratch: keys of B*(L+1) rows (rounded to 256 bytes) + B counters
-    limit = 256 * 1024
+    # scratch: a key line and a count line per row of B*(L+1), a count line
+    # per sequence
+    limit = 2 * 1024 * 1024
     n = ctypes.c_size_t(0)
     assert lib.bq_spec_verify_workspace(4096, 15, 1000, ctypes.byref(n)) == OK and n.value > limit
     assert sv(B=4096, L=15) == SCRATCH_ERR

@@ -93,3 +93,46 @@ def test_spec_verify_all_accepted_and_first_rejected():
     a, n, t = _run(s.logits, s.draft)
     assert a.tolist() == [0, 7, 3, 7, 0, 6]
     assert np.array_equal(n, s.planted[np.arange(B), a])
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("V", [7, 9, 8193, 20011])
+def test_spec_verify_maximum_kinds(dtype, V):
+    """Rows whose maximum is each kind of value the kernel tells apart: a
+    positive or negative normal number (also repeated, and at the first and
+    last index), a subnormal, the most negative finite value, -inf, a zero;
+    rows start at every offset within a 16-byte block (odd V)."""
+    rng = np.random.default_rng(62 + V)
+    fi = np.finfo(dtype)
+    B, L = 3, 6
+    rows = B * (L + 1)
+    lg = (rng.standard_normal((rows, V)) * 3).astype(dtype)
+    sub = fi.smallest_subnormal
+    lg[0] = -np.abs(lg[0]) - 1                          # negative normal maximum
+    lg[0, V // 2] = -0.5
+    lg[1, :] = -np.abs(lg[1]) - 1                       # maximum at the first index
+    lg[1, 0] = -0.25
+    lg[2, :] = -np.abs(lg[2]) - 1                       # maximum at the last index
+    lg[2, V - 1] = -0.125
+    lg[3] = -np.abs(lg[3])                              # subnormal maximum, repeated
+    lg[3, V // 3] = sub * 3
+    lg[3, V - 1] = sub * 3
+    lg[4] = -fi.max                                     # the most negative finite value everywhere
+    lg[5] = -fi.max
+    lg[5, V // 2:] = -np.inf                            # ... and -inf after it
+    lg[6] = -np.inf                                     # -inf everywhere: index 0
+    lg[7] = -np.abs(lg[7]) - 1                          # a zero maximum: -0 first, then +0
+    lg[7, V - 1] = 0.0
+    lg[7, min(3, V - 2)] = -0.0
+    lg[8] = np.abs(lg[8]) + 1                           # repeated positive maximum
+    lg[8, [V - 1, V // 2, 1]] = 7.0
+    lg[9] = -np.abs(lg[9]) - 1                          # -fmax beside a normal maximum
+    lg[9, 0] = -fi.max
+    lg[9, V - 1] = -2.0
+    lg[10, :] = sub                                     # subnormal everywhere
+    lg = lg.reshape(B, L + 1, V)
+    t_ref = oracle.target_tokens(lg)
+    draft = t_ref[:, :L].astype(np.int32).copy()
+    draft[2, 4] += 1
+    print(f"spec maximum kinds V{V} {np.dtype(dtype).name}", flush=True)
+    _check(lg, draft, what=f"maximum kinds V{V}")
