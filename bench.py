@@ -88,7 +88,9 @@ def parse():
                     help="eager launches for rocprofv3 --pmc runs: 'family:KEY' (KEY like u2-asym/gs64/M5: the "
                          "seven shapes), 'decode' (gate and down, M 1..5, 2-bit affine and t5, gs 64), 't5' (t5 "
                          "gs 64 and 128, seven shapes, M 1 and 5), 'qmm' (t5 qmm gs 128 on gate and down, M 32, "
-                         "512, 2048), 'dequant' (bits 1, 2, t5 on gate and down)")
+                         "512, 2048), 'dequant' (bits 1, 2, t5 on gate and down), 'next' (2-bit qmm on gate and "
+                         "down at M 32 and 512, K-split at M 32; t5 repack of 2-bit gate weights; draft "
+                         "verification B1 L4 and B8 L7)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="rocprofv3 counter_collection.csv files of two --launch-set family:KEY runs with "
                          "FETCH_SIZE and WRITE_SIZE; writes profiles/traffic.json")
@@ -366,7 +368,54 @@ def launch_set_specs(name):
     if name == "dequant":
         return [("bq_dequant", f, "asym" if f != "t5" else "t5", 0, s, 64) for f in ("u1", "u2", "t5")
                 for s in ("gate", "down")]
+    if name == "next":
+        # the 1/2-bit prefill product (whole and K-split), the t5 repack of
+        # 2-bit gate weights, and draft verification over the Qwen
+        # vocabulary (B sequences of L draft tokens, fp16 logits)
+        return ([("bq_qmm", "u2", "asym", M, s, 64) for s in ("gate", "down") for M in (32, 512)]
+                + [("bq_qmm_ws", "u2", "asym", 32, s, 64) for s in ("gate", "down")]
+                + [("bq_t5_repack", "u2", "asym", 0, "gate", 128)]
+                + [("bq_spec_decode_verify", "f16", f"B{B}L{L}", 0, "vocab", 0) for B, L in ((1, 4), (8, 7))])
     raise SystemExit(f"unknown launch set {name!r}")
+
+
+def next_row_launch(torch, lib, dev, entry, fmt, variant, shape, gs, h, dst, src):
+    """One eager bq_t5_repack or bq_spec_decode_verify call of the "next"
+    launch set, after the cache-evicting pass; returns the bytes it must
+    read and write."""
+    import ctypes
+
+    import numpy as np
+    import synth
+    if entry == "bq_t5_repack":
+        N, K = synth.PROJECTION_SHAPES[shape]
+        inp = synth.make_inputs(fmt, 1, N, K, gs, variant, seed=0)
+        w = upload(torch, inp.w, dev)
+        o = torch.empty((N, (K // gs) * (gs * 13 // 64)), dtype=torch.uint8, device=dev)
+        flag = torch.empty(1, dtype=torch.int32, device=dev)
+        torch.add(dst, 1.0, out=src)
+        torch.cuda.synchronize()
+        st = lib.bq_t5_repack(w.data_ptr(), o.data_ptr(), N, K, inp.bits, gs, flag.data_ptr(), h)
+        nb = w.numel() * 4 + o.numel()
+    else:
+        B, L = (int(v) for v in variant[1:].split("L"))
+        V = synth.QWEN_VOCAB
+        sp = synth.make_spec_inputs(B, L, V, dtype=np.float16, seed=0)
+        lg, dr = upload(torch, sp.logits, dev), upload(torch, sp.draft, dev)
+        n = ctypes.c_size_t(0)
+        lib.bq_spec_verify_workspace(B, L, V, ctypes.byref(n))
+        ws = torch.zeros(n.value, dtype=torch.uint8, device=dev)
+        a = torch.empty(B, dtype=torch.int32, device=dev)
+        nx = torch.empty(B, dtype=torch.int32, device=dev)
+        torch.add(dst, 1.0, out=src)
+        torch.cuda.synchronize()
+        st = lib.bq_spec_decode_verify(lg.data_ptr(), 1, dr.data_ptr(), B, L, V, a.data_ptr(), nx.data_ptr(), None,
+                                       ws.data_ptr(), n.value, h)
+        nb = lg.numel() * 2
+    if st != 0:
+        raise RuntimeError(f"{entry}: status {st}")
+    torch.cuda.synchronize()
+    return nb
 
 
 def launch_set_run(torch, lib, dev, name):
@@ -381,6 +430,11 @@ def launch_set_run(torch, lib, dev, name):
     h = torch.cuda.current_stream().cuda_stream
     labels, nbytes = [], []
     for entry, fmt, variant, M, shape, gs in launch_set_specs(name):
+        if entry in ("bq_t5_repack", "bq_spec_decode_verify"):
+            nb = next_row_launch(torch, lib, dev, entry, fmt, variant, shape, gs, h, dst, src)
+            labels.append(f"{entry}/{fmt}-{variant}/gs{gs}/M{M}/{shape}")
+            nbytes.append(nb)
+            continue
         N, K = synth.PROJECTION_SHAPES[shape]
         inp = synth.make_inputs(fmt, max(M, 1), N, K, gs, variant, seed=0)
         x, w, s, b = [upload(torch, a, dev) for a in (inp.x, inp.w, inp.scales, inp.biases)]
