@@ -175,6 +175,22 @@ class Call:
         return out
 
 
+class CopyRef:
+    """Reference launch for the roofline: torch's elementwise add of a
+    constant over nbytes/4 fp16 values (reads nbytes/2, writes nbytes/2)."""
+
+    def __init__(self, torch, dev, nbytes):
+        n = max(64, nbytes // 4)
+        self.src = torch.ones(n, dtype=torch.float16, device=dev)
+        self.dst = torch.empty_like(self.src)
+        self.bytes = 4 * n
+        self.torch = torch
+
+    def launch(self, lib, stream):
+        # on the current stream (the capturing one inside capture())
+        self.torch.add(self.src, 1.0, out=self.dst)
+
+
 def upload(torch, a, dev):
     import numpy as np
     if a is None:
@@ -783,6 +799,15 @@ def main():
         achieved = bytes_per_launch / avg_launch / 1e9
         del copies, seq
         torch.cuda.empty_cache()
+        # in-run streaming reference at the same bytes per launch: a plain
+        # elementwise pass (half read, half written) over the same number
+        # of rotating buffers of each shape's size
+        refs = [[CopyRef(torch, dev, c.bytes) for _ in range(ncp)] for c in fam_calls]
+        rseq = [refs[i][j] for j in range(ncp) for i in range(len(fam_calls))]
+        ref_launch = rotation_seconds(torch, lib, rseq, replays=5)
+        ref_bytes = sum(r[0].bytes for r in refs) / len(fam_calls)
+        del refs, rseq
+        torch.cuda.empty_cache()
         result["roofline"] = {
             "bound": "hbm",
             "kernel": f"qmv_kernel family {key} (format-variant / group size / M) over its 7 shapes",
@@ -794,6 +819,11 @@ def main():
             "avg_launch_us": round(avg_launch * 1e6, 3),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
             "share_of_step": round(fam_t.get(dom, 0.0) / tot, 4) if per else None,
+            "stream_ref": {"kind": "torch elementwise add over rotating fp16 buffers of the family's per-shape "
+                                   "bytes (half read, half written), same launch sequence",
+                           "avg_launch_us": round(ref_launch * 1e6, 3),
+                           "GBps": round(ref_bytes / ref_launch / 1e9, 1),
+                           "frac": round(ref_bytes / ref_launch / 1e9 / PEAK_HBM_GBS, 4)},
         }
         if args.suite == "full":
             os.makedirs(os.path.dirname(args.detail_csv), exist_ok=True)
