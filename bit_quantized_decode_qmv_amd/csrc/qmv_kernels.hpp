@@ -10,13 +10,14 @@
 //
 // gfx950 design
 // -------------
-// * One workgroup of 8 waves per CU.  A wave holds four slots of 16 lanes;
-//   the 16 lanes of a slot cover one 1024-code K tile of R = 1, 2 or 4 rows, each
-//   lane one chunk: 64 codes of 1/2-bit words (8 or 16 bytes) or one
-//   13-byte t5 run (a whole 64-group, or half of a 128-group: 65 + 63 codes).
+// * One workgroup of W = 8 waves per CU (12 from M = 3 on the long
+//   shapes).  A wave holds four slots of 16 lanes; the 16 lanes of a slot
+//   cover one 1024-code K tile of R = 1, 2 or 4 rows, each lane one chunk:
+//   64 codes of 1/2-bit words (8 or 16 bytes) or one 13-byte t5 run (a
+//   whole 64-group, or half of a 128-group: 65 + 63 codes).
 // * Work unit = (row-group of R rows, K tile).  A workgroup's units, in the
 //   order of their bytes, are dealt to its slots cyclically (slot k: units
-//   k, k + 32, ...), so at every step its slots read one contiguous stretch
+//   k, k + 4W, ...), so at every step its slots read one contiguous stretch
 //   of its rows; a slot keeps a ring of P units in flight, so HBM reads
 //   overlap the arithmetic without any barrier.  Each unit's partial sums
 //   are reduced over the slot's lanes into LDS, keyed by (row-group, tile),
@@ -64,9 +65,14 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 enum { FMT_U1 = 1, FMT_U2 = 2, FMT_T5 = 5 };
 constexpr int kTile = 1024;        // codes per K tile
 constexpr int kKL = 16;            // lanes per slot (chunks per tile)
-constexpr int kWaves = 8;          // waves per workgroup (one workgroup per CU)
+constexpr int kWaves = 8;          // waves per workgroup at M <= 2 (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = kThreads / kKL;
+// Instances with kWaves3 = 12 waves (three per SIMD) exist too: from M = 3
+// a unit's loop is a chain of LDS reads and dot products that two waves per
+// SIMD do not hide; 2-row units keep their registers within three waves'
+// share.
+constexpr int kWaves3 = 12;
 constexpr int kR = 2;              // rows per row-group of the scale-staging limit (the kernels take R = 1, 2 or 4)
 constexpr int kXD = 36;            // LDS dwords per staged chunk (32-35 used)
 
@@ -494,23 +500,23 @@ struct SbStage {
   int nvec;
 };
 
-template <bool IMPLIED>
+template <bool IMPLIED, int TH>
 __device__ __forceinline__ void sbstage_load(rsrc_t rs, rsrc_t rb, uint32_t lo_al, int nvec, SbStage& st) {
   st.nvec = nvec;
 #pragma unroll
   for (int k = 0; k < kSbRounds; ++k) {
-    const int v = (int)threadIdx.x + k * kThreads;
+    const int v = (int)threadIdx.x + k * TH;
     const int off = (int)((lo_al + 16u * (uint32_t)v) | (v < nvec ? 0u : 0x80000000u));
     st.s[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     if constexpr (!IMPLIED) st.b[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
   }
 }
 
-template <bool IMPLIED, bool F32>
+template <bool IMPLIED, bool F32, int TH>
 __device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl, float ratio) {
 #pragma unroll
   for (int k = 0; k < kSbRounds; ++k) {
-    const int v = (int)threadIdx.x + k * kThreads;
+    const int v = (int)threadIdx.x + k * TH;
     if (F32 && v < st.nvec) {
       float o[16];
 #pragma unroll
@@ -665,8 +671,10 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
 // --------------------------------------------------------------------------
 // The kernel.
 // --------------------------------------------------------------------------
-template <int FMT, int GS, int M, bool IMPLIED, int P, int R>
-__global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
+template <int FMT, int GS, int M, bool IMPLIED, int P, int R, int W>
+__global__ __launch_bounds__(64 * W) void qmv_kernel(QmvParams p) {
+  constexpr int TH = 64 * W;     // threads of the workgroup (W waves)
+  constexpr int NSL = TH / kKL;  // its slots
   using F = Fmt<FMT, GS>;
   constexpr int CS = chunk_stride<M>();
   extern __shared__ uint32_t smem[];
@@ -700,19 +708,19 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   // x of segment 0 first, so that waiting for it never waits for W
   XStage<FMT, GS> xst[kStageRounds];
 #pragma unroll
-  for (int k = 0; k < kStageRounds; ++k) xstage_plan<FMT, GS, M>(p, 0, min(ST, T), tid + k * kThreads, xst[k]);
+  for (int k = 0; k < kStageRounds; ++k) xstage_plan<FMT, GS, M>(p, 0, min(ST, T), tid + k * TH, xst[k]);
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
   SbStage sbst;
   const int sb_size = (p.sb_bytes + 3) & ~3;
-  sbstage_load<IMPLIED>(make_rsrc(p.s, sb_size), make_rsrc(IMPLIED ? p.s : p.b, sb_size), sb_lo_al, sb_nvec, sbst);
+  sbstage_load<IMPLIED, TH>(make_rsrc(p.s, sb_size), make_rsrc(IMPLIED ? p.s : p.b, sb_size), sb_lo_al, sb_nvec, sbst);
 
   auto seg_tiles = [&](int s) { return min(ST, T - s * ST); };
 
   // ---- Units of segment s: u = g * Ts + t (row-group g, tile t), in the
-  // order of their bytes.  Slot k takes units k, k + kSlots, k + 2 kSlots,
+  // order of their bytes.  Slot k takes units k, k + NSL, k + 2 NSL,
   // ..., so at every step the workgroup's slots read one contiguous stretch
-  // of its rows.  Cursor step: kSlots units = dg row-groups + dt tiles.
+  // of its rows.  Cursor step: NSL units = dg row-groups + dt tiles.
   // Every fetch issues the same loads (rows past N and chunks past K read
   // zeros or data that is never used), so the compiler can wait for exactly
   // the ring entry it needs.  Fetches past the last unit use an offset
@@ -722,12 +730,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   uint32_t fwrow = 0, fc0 = 0;
   auto fetch_start = [&](int s) {
     fTs = seg_tiles(s);
-    fdg = kSlots / fTs;
-    fdt = kSlots - fdg * fTs;
+    fdg = NSL / fTs;
+    fdt = NSL - fdg * fTs;
     const int g = slot / fTs;
     ft = slot - g * fTs;
     const int U = NG * fTs;
-    fleft = slot < U ? (U - 1 - slot) / kSlots + 1 : 0;
+    fleft = slot < U ? (U - 1 - slot) / NSL + 1 : 0;
     fwrow = (uint32_t)(base + g * R) * (uint32_t)p.row_bytes;
     fc0 = (uint32_t)(s * ST * kKL + kl);
   };
@@ -829,19 +837,19 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   }
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
-  sbstage_commit<IMPLIED, SBF>(sbst, sbl, p.ratio);
+  sbstage_commit<IMPLIED, SBF, TH>(sbst, sbl, p.ratio);
   lds_barrier();  // x of segment 0, scales and biases staged; table built
 #pragma unroll
   for (int j = kEarly; j < P; ++j) fetch(ring[j]);
 
   for (int s = 0; s < p.nseg; ++s) {
     cTs = seg_tiles(s);
-    cdg = kSlots / cTs;
-    cdt = kSlots - cdg * cTs;
+    cdg = NSL / cTs;
+    cdt = NSL - cdg * cTs;
     cg = slot / cTs;
     ct = slot - cg * cTs;
     const int U = NG * cTs;
-    const int n = slot < U ? (U - 1 - slot) / kSlots + 1 : 0;  // units of this slot
+    const int n = slot < U ? (U - 1 - slot) / NSL + 1 : 0;  // units of this slot
     for (int i = 0; i < n; i += P) {
 #pragma unroll
       for (int j = 0; j < P; ++j) {
@@ -852,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
     if (s + 1 < p.nseg) {
 #pragma unroll
       for (int k = 0; k < kStageRounds; ++k)
-        xstage_plan<FMT, GS, M>(p, (s + 1) * ST, seg_tiles(s + 1), tid + k * kThreads, xst[k]);
+        xstage_plan<FMT, GS, M>(p, (s + 1) * ST, seg_tiles(s + 1), tid + k * TH, xst[k]);
 #pragma unroll
       for (int k = 0; k < kStageRounds; ++k) xstage_load<FMT, GS>(rx, xst[k]);
       fetch_start(s + 1);
@@ -866,7 +874,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(QmvParams p) {
   }
 
   // y = sum over the row's tiles, in tile order, * 2^24
-  for (int idx = tid; idx < NG * R * M; idx += kThreads) {
+  for (int idx = tid; idx < NG * R * M; idx += TH) {
     const int g = idx / (R * M);
     const int rm = idx - g * (R * M);
     const int r = rm / M, m = rm - r * M;

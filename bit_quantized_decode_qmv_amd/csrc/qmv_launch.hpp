@@ -26,13 +26,14 @@ size_t qmv_lds_bytes(int M, int R, int rows_per_wg, int ntiles, int seg_tiles, i
 // many K tiles of x as LDS and the staging tasks (M * tiles * 16 <=
 // kStageRounds * kThreads) allow, split evenly.  Returns false if even R rows
 // per workgroup do not fit.
-bool qmv_geometry(QmvParams& p, int M, int R) {
+bool qmv_geometry(QmvParams& p, int M, int R, int W = kWaves) {
+  const int threads = 64 * W;
   p.ntiles = (p.K + kTile - 1) / kTile;
-  const int max_st = std::min(p.ntiles, kStageRounds * kThreads / (kKL * M));
+  const int max_st = std::min(p.ntiles, kStageRounds * threads / (kKL * M));
   int rows = R * ((p.N + R * kTargetWorkgroups - 1) / (R * kTargetWorkgroups));
   if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
   for (; rows >= R; rows -= R) {
-    if (sb_vectors(rows, p.G) > kSbRounds * kThreads) continue;
+    if (sb_vectors(rows, p.G) > kSbRounds * threads) continue;
     int st = max_st;
     while (st > 0 && qmv_lds_bytes(M, R, rows, p.ntiles, st, p.G) > kLdsBudget) --st;
     if (st == 0) continue;
@@ -46,21 +47,22 @@ bool qmv_geometry(QmvParams& p, int M, int R) {
 }
 
 // Units each slot takes in one segment, at most.
-int units_per_slot(const QmvParams& p, int R) {
+int units_per_slot(const QmvParams& p, int R, int W = kWaves) {
   const int U = ((p.rows_per_wg + R - 1) / R) * p.seg_tiles;
-  return (U + kSlots - 1) / kSlots;
+  const int slots = 64 * W / kKL;
+  return (U + slots - 1) / slots;
 }
 
-template <int FMT, int GS, int M, bool IMPLIED, int P, int R>
+template <int FMT, int GS, int M, bool IMPLIED, int P, int R, int W = kWaves>
 int launch_qmv_p(const QmvParams& p, void* stream) {
-  const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P, R>);
+  const void* fn = reinterpret_cast<const void*>(&qmv_kernel<FMT, GS, M, IMPLIED, P, R, W>);
   static const hipError_t attr =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
   (void)attr;
   const size_t shmem = qmv_lds_bytes(M, R, p.rows_per_wg, p.ntiles, p.seg_tiles, p.G);
   dim3 grid((p.N + p.rows_per_wg - 1) / p.rows_per_wg);
   QmvParams q = p;
-  return launch_kernel(fn, grid, dim3(kThreads), shmem, stream, &q);
+  return launch_kernel(fn, grid, dim3(64 * W), shmem, stream, &q);
 }
 
 // Rows per unit R and units in flight per slot P never change a row's
@@ -83,6 +85,13 @@ int launch_qmv_t(QmvParams p, void* stream) {
   }
   if (qmv_geometry(p, M, 4)) {
     if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
+    // several units per slot from M = 3: three waves per SIMD on 2-row
+    // units (measured 4-6% faster on 2-bit, 1-2% on t5; t5 at M = 5, whose
+    // 2-row units then spill registers, stays on two waves per SIMD)
+    if constexpr (M >= 3 && !(FMT == FMT_T5 && M == 5)) {
+      QmvParams p2 = p;
+      if (qmv_geometry(p2, M, 2, kWaves3)) return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 2, kWaves3>(p2, stream);
+    }
     return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);
   }
   if (!qmv_geometry(p, M, 2)) return BQ_ERR_SHAPE;
