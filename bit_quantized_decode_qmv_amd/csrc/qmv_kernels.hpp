@@ -10,8 +10,8 @@
 //
 // gfx950 design
 // -------------
-// * One workgroup of W = 8 waves per CU (12 from M = 3 on the long
-//   shapes).  A wave holds four slots of 16 lanes; the 16 lanes of a slot
+// * One workgroup of W = 8 or 12 waves per CU (12 with 2-row units on the
+//   long shapes).  A wave holds four slots of 16 lanes; the 16 lanes of a slot
 //   cover one 1024-code K tile of R = 1, 2 or 4 rows, each lane one chunk:
 //   64 codes of 1/2-bit words (8 or 16 bytes) or one 13-byte t5 run (a
 //   whole 64-group, or half of a 128-group: 65 + 63 codes).
@@ -68,8 +68,8 @@ constexpr int kKL = 16;            // lanes per slot (chunks per tile)
 constexpr int kWaves = 8;          // waves per workgroup at M <= 2 (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = kThreads / kKL;
-// Instances with kWaves3 = 12 waves (three per SIMD) exist too: from M = 3
-// a unit's loop is a chain of LDS reads and dot products that two waves per
+// Instances with kWaves3 = 12 waves (three per SIMD) exist too: a unit's
+// loop is a chain of staged-x LDS reads and dot products that two waves per
 // SIMD do not hide; 2-row units keep their registers within three waves'
 // share.
 constexpr int kWaves3 = 12;

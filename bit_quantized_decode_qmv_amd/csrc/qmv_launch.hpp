@@ -85,10 +85,10 @@ int launch_qmv_t(QmvParams p, void* stream) {
   }
   if (qmv_geometry(p, M, 4)) {
     if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
-    // several units per slot from M = 3: three waves per SIMD on 2-row
-    // units (measured 4-6% faster on 2-bit, 1-2% on t5; t5 at M = 5, whose
-    // 2-row units then spill registers, stays on two waves per SIMD)
-    if constexpr (M >= 3 && !(FMT == FMT_T5 && M == 5)) {
+    // several units per slot: three waves per SIMD on 2-row units (measured
+    // 3-9% faster at every M; t5 at M = 5, whose 2-row units then spill
+    // registers, stays on two waves per SIMD)
+    if constexpr (!(FMT == FMT_T5 && M == 5)) {
       QmvParams p2 = p;
       if (qmv_geometry(p2, M, 2, kWaves3)) return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 2, kWaves3>(p2, stream);
     }
