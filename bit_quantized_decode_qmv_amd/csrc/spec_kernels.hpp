@@ -16,11 +16,14 @@
 // thread reads its share of the chunk with 16-byte loads, all issued before
 // the first comparison; the loads are aligned to 16 bytes in memory, so a
 // row that does not start on a 16-byte boundary has its first and last
-// blocks partly outside it (those values are masked; an aligned 16-byte
-// block holding one byte of the row lies in the row's pages).  A workgroup
-// reduces its chunk to one 64-bit key (order-preserving 16/32-bit key of the
-// value above, complement of the index below) and merges it into the row's
-// slot with a 64-bit atomic max.  Then it counts itself done on the
+// blocks partly outside it (those values are replaced by the most negative
+// finite value, the fill; an aligned 16-byte block holding one byte of the
+// row lies in the row's pages).  A workgroup reduces its chunk to one
+// 64-bit key (order-preserving 16/32-bit key of the value above, complement
+// of the index below): with the hardware max when that decides alone (a
+// finite normal maximum other than the fill), else by comparing every
+// value's key.  It merges the key into the row's slot with a 64-bit atomic
+// max.  Then it counts itself done on the
 // row's counter, and the workgroup that completes a row counts the row done
 // on the sequence's counter; the workgroup that completes that count reads
 // the L+1 row keys, writes the outputs and clears the slots and counters, so
@@ -85,7 +88,8 @@ __device__ __forceinline__ unsigned long long spec_pack(uint32_t key, int v) {
 
 // Bit patterns per logits type: the fill that stands for values outside
 // the row (the most negative finite value), the smallest normal magnitude,
-// the magnitude mask, and the value of a key that is not a NaN key.
+// the magnitude mask, and value_of: the value bits a key other than the NaN
+// key stands for (spec_key inverted; zero comes back as +0).
 template <typename T> struct SpecBits;
 template <> struct SpecBits<_Float16> {
   static constexpr uint32_t kFill = 0xFBFFu, kMinNormal = 0x0400u, kAbs = 0x7FFFu;
