@@ -378,18 +378,39 @@ __device__ __forceinline__ void xstage_commit(const XStage<FMT, GS>& st, uint32_
   // the chunk's staging exponent, from the largest |x| of the loaded span
   // (for a t5 128-group half a value or two of the neighbouring half may
   // take part: any exponent is exact as long as staging and epilogue agree)
-  u16x2 am = u16x2{0, 0};
+  // largest |x| = max(largest x, -smallest x), with three-input packed
+  // maximum/minimum (IEEE maximum: the same magnitude bits as an integer
+  // max of |x|, a NaN giving the NaN exponent as before)
+  constexpr int NJ = XSpan<FMT, GS>::TAIL ? 33 : 32;
+  half2_t mx = __builtin_bit_cast(half2_t, X(0)), mn = mx;
 #pragma unroll
-  for (int j = 0; j < (XSpan<FMT, GS>::TAIL ? 33 : 32); ++j)
-    am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2, X(j) & 0x7FFF7FFFu));
-  const int ce = stage_exponent(am[0] > am[1] ? am[0] : am[1]);
+  for (int j = 1; j + 1 < NJ; j += 2) {
+    const half2_t a = __builtin_bit_cast(half2_t, X(j)), b2 = __builtin_bit_cast(half2_t, X(j + 1));
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, a), b2);
+    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, a), b2);
+  }
+  if constexpr (NJ % 2 == 0) {
+    const half2_t a = __builtin_bit_cast(half2_t, X(NJ - 1));
+    mx = __builtin_elementwise_maximum(mx, a);
+    mn = __builtin_elementwise_minimum(mn, a);
+  }
+  const half2_t am2 = __builtin_elementwise_maximum(mx, -mn);
+  const half_t amh = __builtin_elementwise_maximum(am2.x, am2.y);
+  const int ce = stage_exponent(__builtin_bit_cast(uint16_t, amh) & 0x7FFFu);
+  // (x[k0], x[k1]) as one dword: one v_perm_b32 of the two loaded dwords
+  auto PX = [&](int k0_, int k1_) -> uint32_t {
+    const uint32_t sel = ((k0_ & 1) ? 0x0302u : 0x0100u) | ((k1_ & 1) ? 0x07060000u : 0x05040000u);
+    return __builtin_amdgcn_perm(X(k1_ >> 1), X(k0_ >> 1), sel);
+  };
   auto P2 = [&](int k0_, int k1_, int e) -> uint32_t {  // (x[k0], x[k1]) * 2^(ce-e); k < 0 means 0
+    if (k0_ >= 0 && k1_ >= 0) return scale_pair(PX(k0_, k1_), ce - e);
     const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
     const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
     return scale_pair(lo | (hi << 16), ce - e);
   };
   // (x[k0] * 2^(ce-e0), x[k1] * 2^(ce-e1)); k < 0 means 0
   auto P2x = [&](int k0_, int k1_, int e0, int e1) -> uint32_t {
+    if (k0_ >= 0 && k1_ >= 0) return scale_pair2(PX(k0_, k1_), ce - e0, ce - e1);
     const uint32_t lo = k0_ >= 0 ? H(k0_) : 0u;
     const uint32_t hi = k1_ >= 0 ? H(k1_) : 0u;
     return scale_pair2(lo | (hi << 16), ce - e0, ce - e1);
