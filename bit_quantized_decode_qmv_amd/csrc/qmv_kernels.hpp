@@ -902,7 +902,15 @@ __global__ __launch_bounds__(64 * W) void qmv_kernel(QmvParams p) {
     if (g * R + r >= nrow_wg) continue;
     const float* src = part + g * T * (R * M) + rm;
     float v = 0.f;
-    for (int t = 0; t < T; ++t) v += src[t * (R * M)];
+    // eight tiles' loads in flight before their adds (same order of adds)
+    for (int t = 0; t < T; t += 8) {
+      float b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = src[min(t + j, T - 1) * (R * M)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (t + j < T) v += b[j];
+    }
     p.y[(size_t)m * p.N + base + g * R + r] = (half_t)(v * 16777216.0f);
   }
 }
