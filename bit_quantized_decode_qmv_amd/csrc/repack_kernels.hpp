@@ -9,7 +9,9 @@
 // Layout written: t5 row n is (K/gs) groups of ceil(gs/5) bytes; code 5j+i
 // of a group is digit i (least significant first) of the group's byte j,
 // unused digits 0.  One thread per group: it loads the group's code words
-// (2 to 8 dwords), forms the group's 13 or 26 bytes in registers, and the
+// (2 to 8 dwords), turns the codes 3 of a 2-bit word into 2 all at once
+// (the fields with both bits set), forms the group's 13 or 26 bytes in
+// registers (Horner's rule over each byte's digits), and the
 // workgroup's 256 groups -- a contiguous, dword-aligned run of output bytes
 // when K is a multiple of 256 -- go out through LDS as whole dwords.
 #pragma once
@@ -47,19 +49,24 @@ __global__ __launch_bounds__(256) void t5_repack_kernel(RepackParams p) {
     const uint32_t* src = p.w + (size_t)n * p.words_per_row + (size_t)g * NW;
     uint32_t wd[NW];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) wd[i] = src[i];
+    for (int i = 0; i < NW; ++i) {
+      wd[i] = src[i];
+      if constexpr (BITS == 2) {
+        // codes 3 (both bits of a field set) become 2, word-wide
+        const uint32_t three = wd[i] & (wd[i] >> 1) & 0x55555555u;
+        ternary = ternary && three == 0u;
+        wd[i] -= three;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
-      uint32_t byte = 0, pw = 1;
+      // Horner from the last digit: byte = sum of q_t * 3^t
+      uint32_t byte = 0;
 #pragma unroll
-      for (int t = 0; t < 5; ++t) {
+      for (int t = 4; t >= 0; --t) {
         const int c = 5 * j + t;  // code within the group
-        if (c < GS) {
-          const uint32_t qc = (wd[(c * BITS) >> 5] >> ((c * BITS) & 31)) & kMask;
-          ternary = ternary && qc <= 2u;
-          byte += (qc > 2u ? 2u : qc) * pw;
-        }
-        pw *= 3u;
+        const uint32_t qc = c < GS ? (wd[(c * BITS) >> 5] >> ((c * BITS) & 31)) & kMask : 0u;
+        byte = byte * 3u + qc;
       }
       stage[threadIdx.x * GB + j] = (uint8_t)byte;
     }
