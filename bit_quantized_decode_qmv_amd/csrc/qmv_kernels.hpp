@@ -10,8 +10,8 @@
 //
 // gfx950 design
 // -------------
-// * One workgroup of W = 8 or 12 waves per CU (12 with 2-row units on the
-//   long shapes).  A wave holds four slots of 16 lanes; the 16 lanes of a slot
+// * One workgroup of W = 8 or 12 waves per CU (12 on the long shapes: with
+//   4-row units for t5 at M >= 3, 2-row units otherwise).  A wave holds four slots of 16 lanes; the 16 lanes of a slot
 //   cover one 1024-code K tile of R = 1, 2 or 4 rows, each lane one chunk:
 //   64 codes of 1/2-bit words (8 or 16 bytes) or one 13-byte t5 run (a
 //   whole 64-group, or half of a 128-group: 65 + 63 codes).
@@ -70,8 +70,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = kThreads / kKL;
 // Instances with kWaves3 = 12 waves (three per SIMD) exist too: a unit's
 // loop is a chain of staged-x LDS reads and dot products that two waves per
-// SIMD do not hide; 2-row units keep their registers within three waves'
-// share.
+// SIMD do not hide.  Their registers must fit three waves' share (168).
 constexpr int kWaves3 = 12;
 constexpr int kR = 2;              // rows per row-group of the scale-staging limit (the kernels take R = 1, 2 or 4)
 constexpr int kXD = 36;            // LDS dwords per staged chunk (32-35 used)
@@ -362,7 +361,13 @@ __device__ __forceinline__ void xstage_plan(const QmvParams& p, int s0, int Ts, 
 
 template <int FMT, int GS>
 __device__ __forceinline__ void xstage_load(rsrc_t rx, XStage<FMT, GS>& st) {
-  if (!st.wave) return;  // whole waves without a task issue nothing
+  if (!st.wave) {  // whole waves without a task issue nothing
+    // (and hold zeros: otherwise a skipped round would keep the previous
+    // segment's registers live through the whole unit loop)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.v[j] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(st.off + 16u * j), 0, 0);
   if constexpr (XSpan<FMT, GS>::TAIL) st.tail = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(st.off + 128u), 0, 0);

@@ -85,15 +85,16 @@ int launch_qmv_t(QmvParams p, void* stream) {
   }
   if (qmv_geometry(p, M, 4)) {
     if (units_per_slot(p, 4) <= 1) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 4>(p, stream);
-    // several units per slot: three waves per SIMD on 2-row units (measured
-    // 3-9% faster at every M); t5 at M = 5, whose 2-row units spill
-    // registers with two units in flight, keeps one (1.3% faster than two
-    // waves per SIMD on 4-row units)
-    QmvParams p2 = p;
-    if (qmv_geometry(p2, M, 2, kWaves3)) {
-      if constexpr (FMT == FMT_T5 && M == 5) return launch_qmv_p<FMT, GS, M, IMPLIED, 1, 2, kWaves3>(p2, stream);
-      else return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 2, kWaves3>(p2, stream);
+    // several units per slot: three waves per SIMD (measured 3-9% faster at
+    // every M than two), on 4-row units for t5 at M >= 3 (1-5% faster than
+    // 2-row units on gate, up and down; 2-bit is 1-5% slower on them) and
+    // on 2-row units otherwise
+    if constexpr (FMT == FMT_T5 && M >= 3) {
+      QmvParams p4 = p;
+      if (qmv_geometry(p4, M, 4, kWaves3)) return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4, kWaves3>(p4, stream);
     }
+    QmvParams p2 = p;
+    if (qmv_geometry(p2, M, 2, kWaves3)) return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 2, kWaves3>(p2, stream);
     return launch_qmv_p<FMT, GS, M, IMPLIED, 2, 4>(p, stream);
   }
   if (!qmv_geometry(p, M, 2)) return BQ_ERR_SHAPE;
