@@ -39,7 +39,9 @@
 //   (elements below 2^-19 of their chunk's largest excepted), and the
 //   result scales with x.  2^-c multiplies the chunk's product sum.
 // * t5 bytes go through a 256-entry LDS table that holds a byte's five
-//   base-3 digits as 2-bit fields; two bytes fill one dword and five masks
+//   base-3 digits as 2-bit fields (and a second copy with the fields in the
+//   upper half, for the second byte of a pair, so that no shift is needed);
+//   two bytes fill one dword and five masks
 //   give five half2 code pairs.  The run's single last byte is paired with
 //   itself (digits 0/1 and 2/3 in the two halves), so it costs two or three
 //   products instead of five.  13-byte runs are loaded as one dword-aligned
@@ -577,7 +579,7 @@ __device__ __forceinline__ void sbstage_commit(const SbStage& st, uint32_t* sbl,
 // --------------------------------------------------------------------------
 template <int FMT, int GS, int M, int R>
 __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint32_t* xc,
-                                          const uint16_t* lut, const uint32_t (&sh)[R], float (&Pd)[R][M]) {
+                                          const uint32_t* lut, const uint32_t (&sh)[R], float (&Pd)[R][M]) {
   if constexpr (FMT == FMT_U2 || FMT == FMT_U1) {
     // quad q = 4 staged dwords 4q..4q+3 (2-bit: word q/2, pairs 4(q%2)..;
     // 1-bit: word q/4, pairs 4(q%4)..); the next quad's x is read while
@@ -661,7 +663,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
         uint32_t v = lut[b0];
         if (paired) {
           const uint32_t b1 = (rb[r][t1 >> 2] >> (8 * (t1 & 3))) & 0xFFu;
-          v |= (uint32_t)lut[b1] << 16;
+          v |= lut[256 + b1];  // the same fields, upper half
           const uint32_t q0 = v & 0x00030003u, q1 = v & 0x000C000Cu, q2 = v & 0x00300030u,
                          q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
 #pragma unroll
@@ -704,7 +706,7 @@ __global__ __launch_bounds__(64 * W) void qmv_kernel(QmvParams p) {
   using F = Fmt<FMT, GS>;
   constexpr int CS = chunk_stride<M>();
   extern __shared__ uint32_t smem[];
-  __shared__ uint16_t lut[256];
+  __shared__ uint32_t lut[512];  // t5 digit fields: [b] in the low half, [256 + b] in the high
 
   const int ST = p.seg_tiles;
   const int T = p.ntiles;
@@ -859,7 +861,11 @@ __global__ __launch_bounds__(64 * W) void qmv_kernel(QmvParams p) {
 #pragma unroll
   for (int j = 0; j < kEarly; ++j) fetch(ring[j]);
   if constexpr (FMT == FMT_T5) {
-    if (tid < 256) lut[tid] = (uint16_t)(tid < 243 ? t5_fields((uint32_t)tid) : 0u);
+    if (tid < 256) {
+      const uint32_t f = tid < 243 ? t5_fields((uint32_t)tid) : 0u;
+      lut[tid] = f;
+      lut[256 + tid] = f << 16;
+    }
   }
 #pragma unroll
   for (int k = 0; k < kStageRounds; ++k) xstage_commit<FMT, GS, M>(xst[k], xs, xsum);
