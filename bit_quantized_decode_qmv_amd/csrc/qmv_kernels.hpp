@@ -619,7 +619,8 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          float acc = Pd[r][m];
+          // the first product starts from the constant 0 (no register to clear)
+          float acc = q == 0 ? 0.f : Pd[r][m];
           acc = dot2(c4[0], xb[q & 1][m][0], acc);
           acc = dot2(c4[1], xb[q & 1][m][1], acc);
           acc = dot2(c4[2], xb[q & 1][m][2], acc);
@@ -668,7 +669,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
                          q3 = v & 0x00C000C0u, q4 = v & 0x03000300u;
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            float acc = Pd[r][m];
+            float acc = pr == 0 ? 0.f : Pd[r][m];
             acc = dot2(q0, xq[pr & 1][m][0], acc);
             acc = dot2(q1, xq[pr & 1][m][1], acc);
             acc = dot2(q2, xq[pr & 1][m][2], acc);
@@ -683,7 +684,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk<FMT> (&wc)[R], const uint3
           const uint32_t q0 = v & 0x000C0003u, q1 = v & 0x00C00030u, q2 = v & 0x00000300u;
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            float acc = Pd[r][m];
+            float acc = pr == 0 ? 0.f : Pd[r][m];
             acc = dot2(q0, xq[pr & 1][m][0], acc);
             acc = dot2(q1, xq[pr & 1][m][1], acc);
             if constexpr (GS == 128) acc = dot2(q2, xq[pr & 1][m][2], acc);
