@@ -75,3 +75,27 @@ def test_full_size_every_m(fmt, gs, variant, shape):
         assert ok, f"{shape} {fmt} gs{gs} {variant} M{M}: worst err/tol {worst:.3g}"
         for m in range(M):
             assert np.array_equal(y[m].astype(np.float16), single[m]), f"M{M} row {m} != single-row call"
+
+
+@pytest.mark.parametrize("fmt,gs,variant", [("t5", 64, "t5"), ("t5", 128, "t5"), ("u2", 64, "asym"), ("u2", 128, "sym")],
+                         ids=lambda c: str(c))
+@pytest.mark.parametrize("M", [3, 5])
+def test_long_shape_ragged_rows(fmt, gs, variant, M):
+    """A gate-like shape three rows short of a multiple of four (17405 x
+    5120): the 12-wave instances (4-row units for t5 at M >= 3, 2-row units
+    for 2-bit) with a last workgroup of 65 rows, so its last row-group is
+    partial.  Sampled rows plus the last 12, against the oracle, and every
+    row bit for bit against single-row calls."""
+    N, K = 17405, 5120
+    inp = make(fmt, M, N, K, gs, variant, seed=63)
+    rows = np.unique(np.concatenate([sample_rows(N, 64), np.arange(N - 12, N)]))
+    y_ref, mass = oracle.qmv_reference(fmt, inp.x, inp.w, inp.scales, inp.biases, K, gs, rows)
+    xd, wd, sd, bd = dev(inp.x), dev(inp.w), dev(inp.scales), dev(inp.biases)
+    print(f"ragged {fmt} gs{gs} {variant} M{M} N{N}", flush=True)
+    y = to_np(call(fmt, variant, xd, wd, sd, bd, gs)).astype(np.float64)
+    assert np.all(np.isfinite(y))
+    ok, worst = oracle.check_close(y[:, rows], y_ref, mass)
+    assert ok, f"ragged {fmt} gs{gs} {variant} M{M}: worst err/tol {worst:.3g}"
+    for m in range(M):
+        y1 = to_np(call(fmt, variant, xd[m:m + 1].contiguous(), wd, sd, bd, gs))[0]
+        assert np.array_equal(y[m].astype(np.float16), y1), f"M{M} row {m} != single-row call"
